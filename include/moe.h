@@ -1,0 +1,194 @@
+/*
+ * moe.h — C ABI of the routed-expert layer with a cold-expert gather, for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (the "gracetier" write-up, section 1 "The idea"; the GB300
+ * inference write-up's paragraph on the mixture-of-experts design):
+ *   1. a router scores E experts per token and keeps the top k;
+ *   2. a gather copies only the picked COLD experts from pinned host memory
+ *      into their fixed slot of one HBM scratch area, which every layer
+ *      reuses because layers run one after another;
+ *   3. one grouped SwiGLU FFN runs every picked expert, reading hot experts
+ *      from HBM and cold ones from scratch, as if all were resident, and the
+ *      expert outputs are added with the routing weights.
+ *
+ * Conventions for every entry point
+ *   - Returns a moe_status; never throws, never aborts.
+ *   - Arguments are validated on the host before anything is enqueued; on
+ *     any error nothing is enqueued.  moe_last_error() describes the last
+ *     error of the calling thread.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ *     No entry point synchronises the host with the device.  Device faults
+ *     surface at the caller's next synchronisation.
+ *   - "device" pointers must be device-accessible memory (hipMalloc'd,
+ *     or pinned host memory mapped for the device); the library checks them
+ *     with the HIP runtime and returns MOE_ERR_NOT_DEVICE_ACCESSIBLE when a
+ *     pointer is not, or MOE_ERR_INVALID_ARG when its allocation is too small.
+ *   - The caller owns all memory; the library allocates nothing on these
+ *     paths.  Scratch space comes from a caller workspace `ws` of at least
+ *     moe_workspace_bytes() bytes, 256-byte aligned; its contents on entry are
+ *     ignored and it may be reused between calls on the same stream.
+ *   - Calls that share a workspace or a scratch area must be ordered (same
+ *     stream, or events).  Stream order alone makes the scratch safe to
+ *     share across layers: a later layer's gather starts after the earlier
+ *     layer's FFN has finished reading it.
+ *
+ * Layouts
+ *   - Activations x: bf16 bit patterns, row-major [T][H].
+ *   - Router weight: fp32 [E][H]; optional logit bias: fp32 [E].
+ *   - Expert blob (one contiguous block of moe_expert_bytes() bytes per
+ *     expert; MXFP4: FP4 E2M1 codes, two per byte with the even element in the
+ *     low nibble, and one E8M0 scale per 32 consecutive elements along the
+ *     contraction axis, following the OCP MX v1.0 formats):
+ *         w13 codes  [2I][H/2]   rows 0..I-1 gate (w1), rows I..2I-1 up (w3)
+ *         w13 scales [2I][H/32]
+ *         w2  codes  [H][I/2]    down projection
+ *         w2  scales [H][I/32]
+ *   - Residency table slot[E] (int32): slot[e] >= 0 means expert e is hot and
+ *     lives at hot_base + slot[e]*B; slot[e] < 0 means cold, with cold index
+ *     c = -slot[e]-1: its bytes are at host_cold + c*B and it runs from
+ *     scratch + c*B (B = moe_expert_bytes()).
+ *   - Routing output: topk_ids int32 [T][k] and topk_w fp32 [T][k], the k
+ *     picks of each token by decreasing weight (ties: lower expert index).
+ *   - Layer output: [T][H], fp32 (MOE_OUT_F32) or bf16 bits (MOE_OUT_BF16).
+ *
+ * Shape limits: H and I multiples of 128; 1 <= k <= min(E, 32); E <= 1024;
+ * 0 <= T <= 1<<20 (T = 0 enqueues nothing and returns MOE_OK).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,           /* NULL / negative / inconsistent argument */
+    MOE_ERR_UNSUPPORTED_SHAPE = 2,     /* outside the shape limits above */
+    MOE_ERR_MISALIGNED = 3,            /* pointer not aligned as documented */
+    MOE_ERR_NOT_DEVICE_ACCESSIBLE = 4, /* pointer the GPU cannot read or write */
+    MOE_ERR_BAD_RESIDENCY = 5,         /* residency table inconsistent */
+    MOE_ERR_WORKSPACE_TOO_SMALL = 6,   /* ws_bytes < moe_workspace_bytes() */
+    MOE_ERR_HIP = 7                    /* a HIP runtime call or launch failed */
+} moe_status;
+
+typedef enum { MOE_OUT_F32 = 0, MOE_OUT_BF16 = 1 } moe_out_dtype;
+
+/* Model shape: hidden size H, expert FFN width I, experts E, picks k. */
+typedef struct {
+    int32_t hidden;
+    int32_t inter;
+    int32_t n_experts;
+    int32_t top_k;
+} moe_shape;
+
+/* Where one layer's experts live.  All memory is caller-owned.
+ *   slot      device [E] residency table (see Layouts).
+ *   hot_base  device [n_hot][B]; may be NULL when n_hot == 0.
+ *   host_cold device-visible pointer to pinned host memory [n_cold][B]
+ *             (moe_host_alloc()); may be NULL when n_cold == 0.
+ *   scratch   device [n_cold][B]; the cold experts' HBM slots, which may be
+ *             shared by every layer; may be NULL when n_cold == 0. */
+typedef struct {
+    const int32_t *slot;
+    const uint8_t *hot_base;
+    const uint8_t *host_cold;
+    uint8_t *scratch;
+    int32_t n_hot;
+    int32_t n_cold;
+} moe_residency;
+
+/* Human-readable name of a status code (static string). */
+const char *moe_status_string(moe_status st);
+
+/* Detail of the last error returned to the calling thread ("" if none). */
+const char *moe_last_error(void);
+
+/* MOE_OK if the shape is within the limits, else MOE_ERR_UNSUPPORTED_SHAPE
+ * or MOE_ERR_INVALID_ARG (NULL). */
+moe_status moe_shape_check(const moe_shape *s);
+
+/* Bytes of one expert blob: 3*H*I*17/32 (0 if the shape is invalid). */
+size_t moe_expert_bytes(const moe_shape *s);
+
+/* Workspace bytes needed by any entry point for T tokens (0 if invalid). */
+size_t moe_workspace_bytes(const moe_shape *s, int32_t n_tokens);
+
+/* Checks a HOST copy of a residency table: the hot entries must be exactly
+ * 0..n_hot-1 and the cold entries exactly 0..n_cold-1 (each once), with
+ * n_hot + n_cold == E.  Returns MOE_ERR_BAD_RESIDENCY otherwise.  Run it once
+ * per residency change (the fast paths trust the device copy, but still
+ * never read outside [0,n_hot) / [0,n_cold): a bad entry makes that
+ * expert's pairs contribute zero). */
+moe_status moe_residency_check(const moe_shape *s, const int32_t *slot_host,
+                               int32_t n_hot, int32_t n_cold);
+
+/* Allocate `bytes` of pinned host memory mapped for the current device and
+ * return its host address and the device-visible address the kernels use
+ * (the page-locked, device-mapped host buffer that the mapped-host design in
+ * the 96 GB RTX PRO 6000 write-up, "Five layers made the difference", also
+ * installs into its kernel path).  flags: bit 0 = coherent (fine-grained)
+ * mapping, else non-coherent.  Free with moe_host_free(). */
+moe_status moe_host_alloc(size_t bytes, int32_t flags, void **host_ptr, void **device_ptr);
+moe_status moe_host_free(void *host_ptr);
+
+/* Router (a1-a2): logits z[t,e] = sum_h x[t,h]*Wr[e,h] + bias[e] in fp32, then
+ * per token the k largest logits (ties to the lower expert index), listed by
+ * decreasing weight, with softmax weights renormalised over the k picks
+ * (renormalize != 0) or plain softmax probabilities over all E
+ * (renormalize == 0).
+ *   x [T][H] bf16 (16-B aligned), w_router [E][H] fp32 (16-B aligned),
+ *   bias [E] fp32 or NULL, topk_ids [T][k] int32, topk_w [T][k] fp32,
+ *   logits_out [T][E] fp32 or NULL (written when given). */
+moe_status moe_route(const moe_shape *s, int32_t n_tokens, const uint16_t *x,
+                     const float *w_router, const float *bias, int32_t renormalize,
+                     int32_t *topk_ids, float *topk_w, float *logits_out,
+                     void *ws, size_t ws_bytes, void *stream);
+
+/* Pick set (a3): for the (token, pick) pairs in topk_ids, writes
+ *   counts_out [E] int32: number of pairs routed to each expert, and
+ *   cold_out [E+1] int32: cold_out[0] = number m of distinct picked experts
+ *   whose slot is cold, cold_out[1..m] = those experts in increasing order.
+ * Pairs whose id is outside [0,E) are not counted.  slot: device [E]. */
+moe_status moe_pick_set(const moe_shape *s, int32_t n_tokens, const int32_t *topk_ids,
+                        const int32_t *slot, int32_t n_hot, int32_t n_cold,
+                        int32_t *counts_out, int32_t *cold_out,
+                        void *ws, size_t ws_bytes, void *stream);
+
+/* Cold gather (a4): every distinct picked expert e with slot[e] < 0 is
+ * copied whole, once, from host_cold + c*B to scratch + c*B (c = -slot[e]-1),
+ * by a kernel that reads the pinned host memory directly; unpicked slots are
+ * not touched.  No host round trip decides what is copied.  With
+ * r->n_cold == 0 nothing is enqueued. */
+moe_status moe_gather_cold(const moe_shape *s, int32_t n_tokens, const int32_t *topk_ids,
+                           const moe_residency *r, void *ws, size_t ws_bytes, void *stream);
+
+/* Grouped expert FFN and combine (a5-a8): for every pair (t, j) with
+ * e = topk_ids[t][j], y = W2_e (silu(W1_e x_t) * (W3_e x_t)) with fp32
+ * accumulation, and out[t] = sum_j topk_w[t][j] * y_(t,j) added in j order
+ * (no float atomics: the result does not depend on where experts live).
+ * Cold experts are read from their scratch slot, so moe_gather_cold must have
+ * run for these ids.  Pairs with an id outside [0,E) contribute nothing.
+ *   out [T][H]: fp32 or bf16 per out_dtype (16-B aligned). */
+moe_status moe_expert_ffn(const moe_shape *s, int32_t n_tokens, const uint16_t *x,
+                          const int32_t *topk_ids, const float *topk_w,
+                          const moe_residency *r, int32_t out_dtype, void *out,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/* The whole layer (a1-a8): moe_route, then the pick set, the cold gather
+ * (skipped when r->n_cold == 0) and the grouped FFN with the combine, all on
+ * `stream`.  topk_ids / topk_w receive the routing. */
+moe_status moe_layer_forward(const moe_shape *s, int32_t n_tokens, const uint16_t *x,
+                             const float *w_router, const float *bias, int32_t renormalize,
+                             const moe_residency *r, int32_t *topk_ids, float *topk_w,
+                             int32_t out_dtype, void *out,
+                             void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

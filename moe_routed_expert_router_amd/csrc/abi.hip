@@ -1,0 +1,357 @@
+// C ABI entry points: argument and geometry validation on the host, then the
+// kernel launches on the caller's stream.  Nothing is enqueued after a failed
+// check (the 96 GB RTX PRO 6000 write-up, "Five layers made the difference",
+// audits its host pages and pointers and fails startup when the geometry is
+// wrong; the GB300 write-up's flag table records a parameter pattern that
+// "silently matches nothing" — every malformed input here is an explicit
+// status instead).
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512];
+
+moe_status fail(moe_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+moe_status ok() {
+    g_err[0] = 0;
+    return MOE_OK;
+}
+
+moe_status check_shape(const moe_shape *s) {
+    if (!s) return fail(MOE_ERR_INVALID_ARG, "shape is NULL");
+    if (s->hidden <= 0 || s->inter <= 0 || s->n_experts <= 0 || s->top_k <= 0)
+        return fail(MOE_ERR_INVALID_ARG, "shape fields must be positive (H=%d I=%d E=%d k=%d)", s->hidden,
+                    s->inter, s->n_experts, s->top_k);
+    if (s->hidden % 128 || s->inter % 128)
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "H and I must be multiples of 128 (H=%d I=%d)", s->hidden, s->inter);
+    if (s->hidden > (1 << 16) || s->inter > (1 << 16))
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "H and I must be <= 65536");
+    if (s->n_experts > moe::kMaxExperts)
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "E=%d exceeds %d", s->n_experts, moe::kMaxExperts);
+    if (s->top_k > moe::kMaxTopK || s->top_k > s->n_experts)
+        return fail(MOE_ERR_UNSUPPORTED_SHAPE, "k=%d must be <= min(E, %d)", s->top_k, moe::kMaxTopK);
+    return MOE_OK;
+}
+
+moe_status check_tokens(int32_t T) {
+    if (T < 0 || T > (1 << 20)) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "n_tokens=%d outside [0, 2^20]", T);
+    return MOE_OK;
+}
+
+// A pointer the GPU will dereference: not NULL, aligned, known to the HIP
+// runtime as device memory or device-mapped host memory, and (where the runtime
+// reports the allocation's range) with `bytes` bytes inside that allocation.
+moe_status check_ptr(const void *p, size_t bytes, size_t align, const char *name) {
+    if (!p) return fail(MOE_ERR_INVALID_ARG, "%s is NULL", name);
+    if ((uintptr_t)p % align) return fail(MOE_ERR_MISALIGNED, "%s is not %zu-byte aligned", name, align);
+    hipPointerAttribute_t at;
+    hipError_t e = hipPointerGetAttributes(&at, p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(MOE_ERR_NOT_DEVICE_ACCESSIBLE, "%s (%p) is not memory known to HIP (%s)", name, p,
+                    hipGetErrorString(e));
+    }
+    if (at.type == hipMemoryTypeUnregistered)
+        return fail(MOE_ERR_NOT_DEVICE_ACCESSIBLE, "%s (%p) is unregistered host memory", name, p);
+    if (at.type == hipMemoryTypeHost && at.devicePointer == nullptr)
+        return fail(MOE_ERR_NOT_DEVICE_ACCESSIBLE, "%s (%p) is host memory not mapped for the device", name, p);
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    e = hipMemGetAddressRange(&base, &size, const_cast<void *>(p));
+    if (e == hipSuccess && base != nullptr && size > 0) {
+        const uintptr_t b = (uintptr_t)base, q = (uintptr_t)p;
+        if (q < b || q + bytes > b + size)
+            return fail(MOE_ERR_INVALID_ARG, "%s: %zu bytes at %p overrun its allocation (%zu bytes at %p)", name,
+                        bytes, p, size, base);
+    } else {
+        (void)hipGetLastError();
+    }
+    return MOE_OK;
+}
+
+#define TRY(expr)                                   \
+    do {                                            \
+        moe_status _st = (expr);                    \
+        if (_st != MOE_OK) return _st;              \
+    } while (0)
+
+moe_status check_ws(const moe_shape *s, int32_t T, void *ws, size_t ws_bytes) {
+    const size_t need = moe::WsLayout::make(s->hidden, s->inter, s->n_experts, s->top_k, T).total;
+    if (ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+    return check_ptr(ws, need, 256, "ws");
+}
+
+moe_status check_residency(const moe_shape *s, const moe_residency *r) {
+    if (!r) return fail(MOE_ERR_INVALID_ARG, "residency is NULL");
+    if (r->n_hot < 0 || r->n_cold < 0 || r->n_hot + r->n_cold != s->n_experts)
+        return fail(MOE_ERR_BAD_RESIDENCY, "n_hot=%d + n_cold=%d must equal E=%d", r->n_hot, r->n_cold,
+                    s->n_experts);
+    const size_t B = moe::BlobLayout::make(s->hidden, s->inter).bytes;
+    TRY(check_ptr(r->slot, (size_t)s->n_experts * 4, 4, "residency.slot"));
+    if (r->n_hot > 0) TRY(check_ptr(r->hot_base, (size_t)r->n_hot * B, 16, "residency.hot_base"));
+    if (r->n_cold > 0) {
+        TRY(check_ptr(r->host_cold, (size_t)r->n_cold * B, 16, "residency.host_cold"));
+        TRY(check_ptr(r->scratch, (size_t)r->n_cold * B, 16, "residency.scratch"));
+    }
+    return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return MOE_OK;
+}
+
+moe::GroupArgs group_args(const moe_shape *s, int32_t T, const int32_t *ids, const moe_residency *r) {
+    moe::GroupArgs g;
+    g.ids = ids;
+    g.T = T;
+    g.k = s->top_k;
+    g.E = s->n_experts;
+    g.slot = r->slot;
+    g.n_hot = r->n_hot;
+    g.n_cold = r->n_cold;
+    g.hot_base = r->hot_base;
+    g.scratch = r->scratch;
+    g.blob_bytes = moe::BlobLayout::make(s->hidden, s->inter).bytes;
+    return g;
+}
+
+moe_status enqueue_ffn(const moe_shape *s, int32_t T, const uint16_t *x, const int32_t *ids, const float *w,
+                       int32_t out_dtype, void *out, char *ws, const moe::WsLayout &L, hipStream_t st) {
+    moe::FfnArgs a;
+    a.x = x;
+    a.ids = ids;
+    a.w = w;
+    a.T = T;
+    a.H = s->hidden;
+    a.I = s->inter;
+    a.E = s->n_experts;
+    a.k = s->top_k;
+    a.out_bf16 = out_dtype == MOE_OUT_BF16;
+    a.out = out;
+    return hip_status(moe::launch_ffn(a, ws, L, st), "ffn launch");
+}
+
+moe_status check_out(const moe_shape *s, int32_t T, int32_t out_dtype, void *out) {
+    if (out_dtype != MOE_OUT_F32 && out_dtype != MOE_OUT_BF16)
+        return fail(MOE_ERR_INVALID_ARG, "out_dtype %d unknown", out_dtype);
+    return check_ptr(out, (size_t)T * s->hidden * (out_dtype == MOE_OUT_F32 ? 4 : 2), 16, "out");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_string(moe_status st) {
+    switch (st) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+        case MOE_ERR_UNSUPPORTED_SHAPE: return "MOE_ERR_UNSUPPORTED_SHAPE";
+        case MOE_ERR_MISALIGNED: return "MOE_ERR_MISALIGNED";
+        case MOE_ERR_NOT_DEVICE_ACCESSIBLE: return "MOE_ERR_NOT_DEVICE_ACCESSIBLE";
+        case MOE_ERR_BAD_RESIDENCY: return "MOE_ERR_BAD_RESIDENCY";
+        case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    }
+    return "MOE_ERR_UNKNOWN";
+}
+
+const char *moe_last_error(void) { return g_err; }
+
+moe_status moe_shape_check(const moe_shape *s) {
+    TRY(check_shape(s));
+    return ok();
+}
+
+size_t moe_expert_bytes(const moe_shape *s) {
+    if (check_shape(s) != MOE_OK) return 0;
+    return moe::BlobLayout::make(s->hidden, s->inter).bytes;
+}
+
+size_t moe_workspace_bytes(const moe_shape *s, int32_t n_tokens) {
+    if (check_shape(s) != MOE_OK || check_tokens(n_tokens) != MOE_OK) return 0;
+    return moe::WsLayout::make(s->hidden, s->inter, s->n_experts, s->top_k, n_tokens).total;
+}
+
+moe_status moe_residency_check(const moe_shape *s, const int32_t *slot_host, int32_t n_hot, int32_t n_cold) {
+    TRY(check_shape(s));
+    if (!slot_host) return fail(MOE_ERR_INVALID_ARG, "slot_host is NULL");
+    const int E = s->n_experts;
+    if (n_hot < 0 || n_cold < 0 || n_hot + n_cold != E)
+        return fail(MOE_ERR_BAD_RESIDENCY, "n_hot=%d + n_cold=%d must equal E=%d", n_hot, n_cold, E);
+    static thread_local unsigned char seen[2 * moe::kMaxExperts];
+    memset(seen, 0, sizeof(seen));
+    for (int e = 0; e < E; ++e) {
+        const int32_t v = slot_host[e];
+        if (v >= 0) {
+            if (v >= n_hot || seen[v]) return fail(MOE_ERR_BAD_RESIDENCY, "expert %d: hot index %d invalid or repeated", e, v);
+            seen[v] = 1;
+        } else {
+            const int64_t c = -(int64_t)v - 1;
+            if (c >= n_cold || seen[moe::kMaxExperts + c])
+                return fail(MOE_ERR_BAD_RESIDENCY, "expert %d: cold slot %lld invalid or repeated", e, (long long)c);
+            seen[moe::kMaxExperts + c] = 1;
+        }
+    }
+    return ok();
+}
+
+moe_status moe_host_alloc(size_t bytes, int32_t flags, void **host_ptr, void **device_ptr) {
+    if (!host_ptr || !device_ptr || bytes == 0) return fail(MOE_ERR_INVALID_ARG, "bad moe_host_alloc arguments");
+    *host_ptr = nullptr;
+    *device_ptr = nullptr;
+    const unsigned f = hipHostMallocMapped | hipHostMallocPortable |
+                       ((flags & 1) ? hipHostMallocCoherent : hipHostMallocNonCoherent);
+    void *h = nullptr;
+    hipError_t e = hipHostMalloc(&h, bytes, f);
+    if (e != hipSuccess) return hip_status(e, "hipHostMalloc");
+    void *d = nullptr;
+    e = hipHostGetDevicePointer(&d, h, 0);
+    if (e != hipSuccess) {
+        (void)hipHostFree(h);
+        return hip_status(e, "hipHostGetDevicePointer");
+    }
+    *host_ptr = h;
+    *device_ptr = d;
+    return ok();
+}
+
+moe_status moe_host_free(void *host_ptr) {
+    if (!host_ptr) return fail(MOE_ERR_INVALID_ARG, "host_ptr is NULL");
+    TRY(hip_status(hipHostFree(host_ptr), "hipHostFree"));
+    return ok();
+}
+
+moe_status moe_route(const moe_shape *s, int32_t T, const uint16_t *x, const float *w_router, const float *bias,
+                     int32_t renormalize, int32_t *topk_ids, float *topk_w, float *logits_out, void *ws,
+                     size_t ws_bytes, void *stream) {
+    TRY(check_shape(s));
+    TRY(check_tokens(T));
+    if (T == 0) return ok();
+    const int H = s->hidden, E = s->n_experts, k = s->top_k;
+    TRY(check_ptr(x, (size_t)T * H * 2, 16, "x"));
+    TRY(check_ptr(w_router, (size_t)E * H * 4, 16, "w_router"));
+    if (bias) TRY(check_ptr(bias, (size_t)E * 4, 4, "bias"));
+    TRY(check_ptr(topk_ids, (size_t)T * k * 4, 4, "topk_ids"));
+    TRY(check_ptr(topk_w, (size_t)T * k * 4, 4, "topk_w"));
+    if (logits_out) TRY(check_ptr(logits_out, (size_t)T * E * 4, 4, "logits_out"));
+    TRY(check_ws(s, T, ws, ws_bytes));
+    const moe::WsLayout L = moe::WsLayout::make(H, s->inter, E, k, T);
+    float *z = logits_out ? logits_out : reinterpret_cast<float *>(static_cast<char *>(ws) + L.logits);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    TRY(hip_status(moe::launch_route_logits(x, w_router, bias, T, H, E, z, st), "router logits launch"));
+    TRY(hip_status(moe::launch_topk(z, T, E, k, renormalize != 0, topk_ids, topk_w, st), "top-k launch"));
+    return ok();
+}
+
+moe_status moe_pick_set(const moe_shape *s, int32_t T, const int32_t *topk_ids, const int32_t *slot, int32_t n_hot,
+                        int32_t n_cold, int32_t *counts_out, int32_t *cold_out, void *ws, size_t ws_bytes,
+                        void *stream) {
+    TRY(check_shape(s));
+    TRY(check_tokens(T));
+    const int E = s->n_experts, k = s->top_k;
+    if (n_hot < 0 || n_cold < 0 || n_hot + n_cold != E)
+        return fail(MOE_ERR_BAD_RESIDENCY, "n_hot=%d + n_cold=%d must equal E=%d", n_hot, n_cold, E);
+    if (T > 0) TRY(check_ptr(topk_ids, (size_t)T * k * 4, 4, "topk_ids"));
+    TRY(check_ptr(slot, (size_t)E * 4, 4, "slot"));
+    TRY(check_ptr(counts_out, (size_t)E * 4, 4, "counts_out"));
+    TRY(check_ptr(cold_out, (size_t)(E + 1) * 4, 4, "cold_out"));
+    TRY(check_ws(s, T, ws, ws_bytes));
+    const moe::WsLayout L = moe::WsLayout::make(s->hidden, s->inter, E, k, T);
+    char *w = static_cast<char *>(ws);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    moe_residency r;
+    r.slot = slot;
+    r.n_hot = n_hot;
+    r.n_cold = n_cold;
+    // only the index ranges matter here: the address table is not used
+    r.hot_base = reinterpret_cast<const uint8_t *>(w);
+    r.scratch = reinterpret_cast<uint8_t *>(w);
+    r.host_cold = nullptr;
+    TRY(hip_status(moe::launch_group(group_args(s, T, topk_ids, &r), w, L, st), "pick-set launch"));
+    TRY(hip_status(moe::launch_pick_set_out(w, L, E, counts_out, cold_out, st), "pick-set output launch"));
+    return ok();
+}
+
+moe_status moe_gather_cold(const moe_shape *s, int32_t T, const int32_t *topk_ids, const moe_residency *r, void *ws,
+                           size_t ws_bytes, void *stream) {
+    TRY(check_shape(s));
+    TRY(check_tokens(T));
+    TRY(check_residency(s, r));
+    if (T == 0 || r->n_cold == 0) return ok();
+    TRY(check_ptr(topk_ids, (size_t)T * s->top_k * 4, 4, "topk_ids"));
+    TRY(check_ws(s, T, ws, ws_bytes));
+    const moe::WsLayout L = moe::WsLayout::make(s->hidden, s->inter, s->n_experts, s->top_k, T);
+    char *w = static_cast<char *>(ws);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const moe::GroupArgs g = group_args(s, T, topk_ids, r);
+    TRY(hip_status(moe::launch_group(g, w, L, st), "pick-set launch"));
+    TRY(hip_status(moe::launch_gather(r->host_cold, r->scratch, g.blob_bytes, r->slot, w, L, st), "gather launch"));
+    return ok();
+}
+
+moe_status moe_expert_ffn(const moe_shape *s, int32_t T, const uint16_t *x, const int32_t *topk_ids,
+                          const float *topk_w, const moe_residency *r, int32_t out_dtype, void *out, void *ws,
+                          size_t ws_bytes, void *stream) {
+    TRY(check_shape(s));
+    TRY(check_tokens(T));
+    TRY(check_residency(s, r));
+    if (T == 0) return ok();
+    const int k = s->top_k;
+    TRY(check_ptr(x, (size_t)T * s->hidden * 2, 16, "x"));
+    TRY(check_ptr(topk_ids, (size_t)T * k * 4, 4, "topk_ids"));
+    TRY(check_ptr(topk_w, (size_t)T * k * 4, 4, "topk_w"));
+    TRY(check_out(s, T, out_dtype, out));
+    TRY(check_ws(s, T, ws, ws_bytes));
+    const moe::WsLayout L = moe::WsLayout::make(s->hidden, s->inter, s->n_experts, k, T);
+    char *w = static_cast<char *>(ws);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    TRY(hip_status(moe::launch_group(group_args(s, T, topk_ids, r), w, L, st), "pick-set launch"));
+    TRY(enqueue_ffn(s, T, x, topk_ids, topk_w, out_dtype, out, w, L, st));
+    return ok();
+}
+
+moe_status moe_layer_forward(const moe_shape *s, int32_t T, const uint16_t *x, const float *w_router,
+                             const float *bias, int32_t renormalize, const moe_residency *r, int32_t *topk_ids,
+                             float *topk_w, int32_t out_dtype, void *out, void *ws, size_t ws_bytes,
+                             void *stream) {
+    TRY(check_shape(s));
+    TRY(check_tokens(T));
+    TRY(check_residency(s, r));
+    if (T == 0) return ok();
+    const int H = s->hidden, E = s->n_experts, k = s->top_k;
+    TRY(check_ptr(x, (size_t)T * H * 2, 16, "x"));
+    TRY(check_ptr(w_router, (size_t)E * H * 4, 16, "w_router"));
+    if (bias) TRY(check_ptr(bias, (size_t)E * 4, 4, "bias"));
+    TRY(check_ptr(topk_ids, (size_t)T * k * 4, 4, "topk_ids"));
+    TRY(check_ptr(topk_w, (size_t)T * k * 4, 4, "topk_w"));
+    TRY(check_out(s, T, out_dtype, out));
+    TRY(check_ws(s, T, ws, ws_bytes));
+    const moe::WsLayout L = moe::WsLayout::make(H, s->inter, E, k, T);
+    char *w = static_cast<char *>(ws);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    float *z = reinterpret_cast<float *>(w + L.logits);
+    TRY(hip_status(moe::launch_route_logits(x, w_router, bias, T, H, E, z, st), "router logits launch"));
+    TRY(hip_status(moe::launch_topk(z, T, E, k, renormalize != 0, topk_ids, topk_w, st), "top-k launch"));
+    const moe::GroupArgs g = group_args(s, T, topk_ids, r);
+    TRY(hip_status(moe::launch_group(g, w, L, st), "pick-set launch"));
+    if (r->n_cold > 0)
+        TRY(hip_status(moe::launch_gather(r->host_cold, r->scratch, g.blob_bytes, r->slot, w, L, st),
+                       "gather launch"));
+    TRY(enqueue_ffn(s, T, x, topk_ids, topk_w, out_dtype, out, w, L, st));
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,142 @@
+// Shared device helpers and the workspace / blob layout of the HIP path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+
+// ------------------------------ expert blob --------------------------------
+// One contiguous blob per expert (MXFP4, two e2m1 codes per byte, even element
+// in the low nibble, one e8m0 scale per 32 elements along the contraction):
+//   w13 codes [2I][H/2] | w13 scales [2I][H/32] | w2 codes [H][I/2] | w2 scales [H][I/32]
+struct BlobLayout {
+    size_t w13_codes, w13_scales, w2_codes, w2_scales, bytes;
+    __host__ __device__ static BlobLayout make(int H, int I) {
+        BlobLayout b;
+        size_t h = (size_t)H, i = (size_t)I;
+        b.w13_codes = 0;
+        b.w13_scales = b.w13_codes + 2 * i * (h / 2);
+        b.w2_codes = b.w13_scales + 2 * i * (h / 32);
+        b.w2_scales = b.w2_codes + h * (i / 2);
+        b.bytes = b.w2_scales + h * (i / 32);
+        return b;
+    }
+};
+
+// ------------------------------- workspace ---------------------------------
+// Regions of the caller's workspace for T tokens (all 256-byte aligned).
+struct WsLayout {
+    size_t logits;     // float [T][E]
+    size_t status;     // int32 [16]: [0] invalid-pair count, [1] bad-residency count
+    size_t nuniq;      // int32 [4]: [0] distinct experts U, [1] picked-cold count
+    size_t uniq;       // int32 [E]: distinct picked experts, increasing
+    size_t ucnt;       // int32 [E]: pairs per distinct expert
+    size_t uoff;       // int32 [E+1]: start of each expert's run in plist
+    size_t uptr;       // uint64 [E]: blob address of each distinct expert (0: skip)
+    size_t cold;       // int32 [E]: picked cold experts, increasing
+    size_t counts;     // int32 [E]: pairs per expert id
+    size_t hist;       // int32 [nchunks][E+1]: per-chunk counts (+ bad ids), then chunk bases
+    size_t rank;       // int32 [P]: rank of a pair among its chunk's pairs of that expert
+    size_t plist;      // int32 [P]: pair ids t*k+j grouped by expert, increasing inside
+    size_t hbuf;       // uint16 [2][P][I]: SwiGLU output split as bf16 hi and lo parts
+    size_t ybuf;       // float [P][H]: per-pair expert outputs
+    size_t total;
+    int nchunks;
+
+    static constexpr int kChunk = 256;   // pairs per grouping chunk
+
+    static size_t up(size_t v) { return (v + 255) & ~(size_t)255; }
+    static WsLayout make(int H, int I, int E, int k, int T) {
+        WsLayout w;
+        size_t P = (size_t)T * k;
+        w.nchunks = (int)((P + kChunk - 1) / kChunk);
+        size_t o = 0;
+        auto take = [&](size_t bytes) { size_t r = o; o += up(bytes > 0 ? bytes : 1); return r; };
+        w.logits = take((size_t)T * E * 4);
+        w.status = take(16 * 4);
+        w.nuniq = take(4 * 4);
+        w.uniq = take((size_t)E * 4);
+        w.ucnt = take((size_t)E * 4);
+        w.uoff = take((size_t)(E + 1) * 4);
+        w.uptr = take((size_t)E * 8);
+        w.cold = take((size_t)E * 4);
+        w.counts = take((size_t)E * 4);
+        w.hist = take((size_t)w.nchunks * (E + 1) * 4);
+        w.rank = take(P * 4);
+        w.plist = take(P * 4);
+        w.hbuf = take(2 * P * (size_t)I * 2);
+        w.ybuf = take(P * (size_t)H * 4);
+        w.total = o;
+        return w;
+    }
+};
+
+// Device view of the grouped pick set, resolved from a workspace base.
+struct GroupView {
+    const int32_t *nuniq;   // [0] U, [1] picked-cold count
+    const int32_t *uniq;
+    const int32_t *ucnt;
+    const int32_t *uoff;
+    const uint64_t *uptr;
+    const int32_t *plist;
+    const int32_t *cold;
+};
+
+// ------------------------------ numerics -----------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+    return __uint_as_float(b << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// e8m0 scale byte -> fp32 value 2^(b-127); 0 is the subnormal 2^-127, 255 NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
+    uint32_t bits = (b == 0u) ? 0x00400000u : ((b == 255u) ? 0x7fc00000u : (b << 23));
+    return __uint_as_float(bits);
+}
+
+// Eight e2m1 codes (one dword, element 2i in the low nibble of byte i) times a
+// scale, as eight bf16 values in element order (exact for normal results).
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t w, float scale) {
+    bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+    bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+    bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+    bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+    bf16x8 r;
+    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+    return r;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float silu(float g) {
+    return g / (1.0f + __expf(-g));
+}
+
+}  // namespace moe

@@ -1,0 +1,194 @@
+// Pick set / grouping (a3): which experts the router picked, the (token, pick)
+// pairs of each, and the picked cold experts.  The gracetier write-up (section
+// 1) has one small kernel look at the router's picks; here that look is these
+// three small kernels, and nothing goes back to the host.
+//
+// Pairs p = t*k + j are cut into chunks of 256.  Per chunk: a histogram over
+// experts and each pair's rank among the chunk's earlier pairs of the same
+// expert.  One block then turns the histograms into per-expert runs (stable:
+// inside a run pairs keep increasing p), the distinct-expert list, the
+// blob-address table and the picked-cold list.  A last pass scatters pair ids.
+#include "kernels.hpp"
+
+namespace moe {
+
+constexpr int kChunk = WsLayout::kChunk;
+
+// hist row layout: [E] per-expert counts then [1] count of out-of-range ids.
+__global__ __launch_bounds__(kChunk) void group_hist(const int32_t *__restrict__ ids, int P, int E,
+                                                     int32_t *__restrict__ hist,
+                                                     int32_t *__restrict__ rank) {
+    __shared__ int32_t cnt[kMaxExperts + 1];
+    __shared__ int32_t sid[kChunk];
+    const int tid = threadIdx.x;
+    const int p = blockIdx.x * kChunk + tid;
+    for (int i = tid; i <= E; i += kChunk) cnt[i] = 0;
+    int e = -1;
+    if (p < P) {
+        e = ids[p];
+        if (e < 0 || e >= E) e = -2;   // out of range: counted, then ignored
+    }
+    sid[tid] = e;
+    __syncthreads();
+    if (e >= 0) {
+        atomicAdd(&cnt[e], 1);
+        int r = 0;
+        for (int q = 0; q < tid; ++q) r += (sid[q] == e);
+        rank[p] = r;
+    } else if (e == -2) {
+        atomicAdd(&cnt[E], 1);
+    }
+    __syncthreads();
+    int32_t *row = hist + (size_t)blockIdx.x * (E + 1);
+    for (int i = tid; i <= E; i += kChunk) row[i] = cnt[i];
+}
+
+// Exclusive scan across a 1024-thread block; returns the block total in *tot.
+__device__ int block_exscan(int v, int *lds, int *tot) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int inc = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(inc, off);
+        if (lane >= off) inc += o;
+    }
+    if (lane == 63) lds[wave] = inc;
+    __syncthreads();
+    if (wave == 0) {
+        int w = (lane < 16) ? lds[lane] : 0;
+        int wi = w;
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+            const int o = __shfl_up(wi, off);
+            if (lane >= off) wi += o;
+        }
+        if (lane < 16) lds[16 + lane] = wi - w;
+        if (lane == 15) lds[32] = wi;
+    }
+    __syncthreads();
+    const int r = lds[16 + wave] + inc - v;
+    *tot = lds[32];
+    __syncthreads();
+    return r;
+}
+
+__global__ __launch_bounds__(1024) void group_scan(int nchunks, int E, const int32_t *__restrict__ slot,
+                                                   int n_hot, int n_cold, const uint8_t *hot_base,
+                                                   const uint8_t *scratch, size_t blob_bytes,
+                                                   int32_t *__restrict__ hist, int32_t *__restrict__ counts,
+                                                   int32_t *__restrict__ nuniq, int32_t *__restrict__ uniq,
+                                                   int32_t *__restrict__ ucnt, int32_t *__restrict__ uoff,
+                                                   uint64_t *__restrict__ uptr, int32_t *__restrict__ cold,
+                                                   int32_t *__restrict__ status) {
+    __shared__ int lds[40];
+    const int e = threadIdx.x;
+    const int stride = E + 1;
+    int total = 0;
+    if (e < E) {
+        for (int c = 0; c < nchunks; ++c) {
+            const int h = hist[(size_t)c * stride + e];
+            hist[(size_t)c * stride + e] = total;
+            total += h;
+        }
+    }
+    const bool is_exp = e < E;
+    const int cnt = is_exp ? total : 0;
+    int ntot;
+    const int off = block_exscan(cnt, lds, &ntot);
+    // residency: never point outside [0, n_hot) / [0, n_cold)
+    int s = 0;
+    bool ok = false;
+    if (is_exp) {
+        s = slot[e];
+        ok = (s >= 0) ? (s < n_hot && hot_base != nullptr)
+                      : (-s - 1 < n_cold && scratch != nullptr);
+    }
+    const bool picked = cnt > 0;
+    int nu;
+    const int ui = block_exscan(picked ? 1 : 0, lds, &nu);
+    const bool is_cold = picked && ok && s < 0;
+    int nc;
+    const int ci = block_exscan(is_cold ? 1 : 0, lds, &nc);
+    int nbad;
+    block_exscan((picked && !ok) ? 1 : 0, lds, &nbad);
+    if (is_exp) {
+        counts[e] = cnt;
+        if (picked) {
+            uniq[ui] = e;
+            ucnt[ui] = cnt;
+            uoff[ui] = off;
+            uint64_t a = 0;
+            if (ok) {
+                a = (s >= 0) ? (uint64_t)(hot_base + (size_t)s * blob_bytes)
+                             : (uint64_t)(scratch + (size_t)(-s - 1) * blob_bytes);
+            }
+            uptr[ui] = a;
+        }
+        if (is_cold) cold[ci] = e;
+        for (int c = 0; c < nchunks; ++c) hist[(size_t)c * stride + e] += off;
+    }
+    if (e == 0) {
+        int bad = 0;   // out-of-range pair count
+        for (int c = 0; c < nchunks; ++c) bad += hist[(size_t)c * stride + E];
+        status[0] = bad;
+        nuniq[0] = nu;
+        nuniq[1] = nc;
+        status[1] = nbad;
+        uoff[nu] = ntot;
+    }
+}
+
+__global__ __launch_bounds__(kChunk) void group_place(const int32_t *__restrict__ ids, int P, int E,
+                                                      const int32_t *__restrict__ hist,
+                                                      const int32_t *__restrict__ rank,
+                                                      int32_t *__restrict__ plist) {
+    const int p = blockIdx.x * kChunk + threadIdx.x;
+    if (p >= P) return;
+    const int e = ids[p];
+    if (e < 0 || e >= E) return;
+    plist[hist[(size_t)blockIdx.x * (E + 1) + e] + rank[p]] = p;
+}
+
+hipError_t launch_group(const GroupArgs &a, char *ws, const WsLayout &L, hipStream_t st) {
+    const int P = a.T * a.k;
+    int32_t *hist = reinterpret_cast<int32_t *>(ws + L.hist);
+    int32_t *rank = reinterpret_cast<int32_t *>(ws + L.rank);
+    if (L.nchunks > 0) {
+        hipLaunchKernelGGL(group_hist, dim3(L.nchunks), dim3(kChunk), 0, st, a.ids, P, a.E, hist, rank);
+    }
+    hipLaunchKernelGGL(group_scan, dim3(1), dim3(1024), 0, st, L.nchunks, a.E, a.slot, a.n_hot, a.n_cold,
+                       a.hot_base, a.scratch, a.blob_bytes, hist,
+                       reinterpret_cast<int32_t *>(ws + L.counts), reinterpret_cast<int32_t *>(ws + L.nuniq),
+                       reinterpret_cast<int32_t *>(ws + L.uniq), reinterpret_cast<int32_t *>(ws + L.ucnt),
+                       reinterpret_cast<int32_t *>(ws + L.uoff), reinterpret_cast<uint64_t *>(ws + L.uptr),
+                       reinterpret_cast<int32_t *>(ws + L.cold), reinterpret_cast<int32_t *>(ws + L.status));
+    if (L.nchunks > 0) {
+        hipLaunchKernelGGL(group_place, dim3(L.nchunks), dim3(kChunk), 0, st, a.ids, P, a.E, hist, rank,
+                           reinterpret_cast<int32_t *>(ws + L.plist));
+    }
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(1024) void pick_set_out(const int32_t *__restrict__ counts,
+                                                     const int32_t *__restrict__ nuniq,
+                                                     const int32_t *__restrict__ cold, int E,
+                                                     int32_t *__restrict__ counts_out,
+                                                     int32_t *__restrict__ cold_out) {
+    const int m = nuniq[1];
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        counts_out[e] = counts[e];
+        cold_out[1 + e] = (e < m) ? cold[e] : -1;
+    }
+    if (threadIdx.x == 0) cold_out[0] = m;
+}
+
+hipError_t launch_pick_set_out(const char *ws, const WsLayout &L, int E, int32_t *counts_out,
+                               int32_t *cold_out, hipStream_t st) {
+    hipLaunchKernelGGL(pick_set_out, dim3(1), dim3(1024), 0, st,
+                       reinterpret_cast<const int32_t *>(ws + L.counts),
+                       reinterpret_cast<const int32_t *>(ws + L.nuniq),
+                       reinterpret_cast<const int32_t *>(ws + L.cold), E, counts_out, cold_out);
+    return hipGetLastError();
+}
+
+}  // namespace moe

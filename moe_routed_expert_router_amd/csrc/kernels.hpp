@@ -1,0 +1,48 @@
+// Internal launchers of the HIP path (one translation unit per kernel family).
+#pragma once
+
+#include "common.hpp"
+
+namespace moe {
+
+// Router logits z[T][E] = x Wr^T + bias (fp32 accumulation).
+hipError_t launch_route_logits(const uint16_t *x, const float *wr, const float *bias,
+                               int T, int H, int E, float *z, hipStream_t st);
+
+// Top-k selection and softmax weights from logits z[T][E].
+hipError_t launch_topk(const float *z, int T, int E, int k, int renorm,
+                       int32_t *ids, float *w, hipStream_t st);
+
+// Pick set / grouping of the T*k pairs; fills the workspace regions of WsLayout.
+struct GroupArgs {
+    const int32_t *ids;
+    int T, k, E;
+    const int32_t *slot;
+    int n_hot, n_cold;
+    const uint8_t *hot_base;
+    const uint8_t *scratch;
+    size_t blob_bytes;
+};
+hipError_t launch_group(const GroupArgs &a, char *ws, const WsLayout &L, hipStream_t st);
+
+// Copies counts [E] and the picked-cold list [E+1] out of a grouped workspace.
+hipError_t launch_pick_set_out(const char *ws, const WsLayout &L, int E,
+                               int32_t *counts_out, int32_t *cold_out, hipStream_t st);
+
+// Copies the picked cold experts host -> scratch.
+hipError_t launch_gather(const uint8_t *host_cold, uint8_t *scratch, size_t blob_bytes,
+                         const int32_t *slot, const char *ws, const WsLayout &L,
+                         hipStream_t st);
+
+// Grouped SwiGLU FFN over the grouped pairs and the weighted combine into out.
+struct FfnArgs {
+    const uint16_t *x;
+    const int32_t *ids;
+    const float *w;
+    int T, H, I, E, k;
+    int out_bf16;
+    void *out;
+};
+hipError_t launch_ffn(const FfnArgs &a, char *ws, const WsLayout &L, hipStream_t st);
+
+}  // namespace moe
