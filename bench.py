@@ -1,0 +1,358 @@
+"""Benchmark of the routed-expert layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one pass of the whole layer (router, pick set, cold gather when
+experts are cold, grouped SwiGLU FFN, combine) over one batch of synthetic
+tokens, through the C ABI.  The headline workload is one decode token through
+one layer with all 384 MXFP4 experts resident (4096 hidden, 2048 expert width,
+top-6).  Steps rotate over a pool of token batches so consecutive steps pick
+different experts and the 256 MB Infinity Cache cannot serve repeated weight
+bytes; the timed steps are replayed from a HIP graph captured over the pool.
+
+Besides the one JSON line on stdout (rank 0), per-kernel durations come from
+HIP events the library records around its own launches (moe_profile_*), in
+a separate eager pass of the same steps, and the CPU oracle is timed on a
+bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routed-expert layer tokens/s + achieved HBM & host-link GB/s at batch 1/8/32"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
+LINK_PEAK_GBS = 64.0             # PCIe Gen5 x16, one direction
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "moe_routed_expert_router_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str) -> float | None:
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken from the current kernel sources (else None)."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Workload:
+    """Device inputs for `reps` batches of one workload, resident as it says."""
+
+    def __init__(self, name: str, reps: int):
+        import torch
+        import moe_routed_expert_router_amd as moe
+        from synth import gen
+        from tests.gpu_setup import Layer
+        self.wl = gen.workload(name)
+        self.reps = reps
+        self.Tb = self.wl.tokens
+        self.layer = Layer(self.wl, T=self.Tb * reps)
+        L = self.layer
+        self.outs = [torch.empty((self.Tb, L.H), dtype=torch.float32, device="cuda") for _ in range(reps)]
+        self.ids = [torch.empty((self.Tb, L.k), dtype=torch.int32, device="cuda") for _ in range(reps)]
+        self.ws_ = [torch.empty((self.Tb, L.k), dtype=torch.float32, device="cuda") for _ in range(reps)]
+        self.ws = torch.empty(moe.moe_workspace_bytes(L.shape, self.Tb), dtype=torch.uint8, device="cuda")
+
+    def step(self, i: int, stream=None):
+        import moe_routed_expert_router_amd as moe
+        L = self.layer
+        r = i % self.reps
+        x = L.x[r * self.Tb:(r + 1) * self.Tb]
+        moe.moe_layer_forward(L.shape, x, L.wr, L.bias, True, L.residency, self.ids[r], self.ws_[r],
+                              self.outs[r], self.ws, stream)
+
+    def picks(self):
+        return np.concatenate([t.cpu().numpy() for t in self.ids])
+
+    def close(self):
+        self.layer.close()
+
+
+def time_steps(w: Workload, steps: int, warmup: int, use_graph: bool):
+    """Wall time of about `steps` whole-layer steps (rounded up to whole
+    replays of the pool); returns (seconds, steps timed, graph used)."""
+    import torch
+    for i in range(warmup):
+        w.step(i)
+    torch.cuda.synchronize()
+    graph = None
+    if use_graph:
+        try:
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=s, capture_error_mode="relaxed"):
+                for i in range(w.reps):
+                    w.step(i, stream=s)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+        except Exception as e:  # capture unsupported: time eagerly instead
+            log(f"graph capture failed ({e}); timing eager launches")
+            graph = None
+            torch.cuda.synchronize()
+    if graph is not None:
+        n_rep = max(1, -(-steps // w.reps))
+        steps = n_rep * w.reps
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n_rep):
+            graph.replay()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, steps, True
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        w.step(i)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, steps, False
+
+
+def profile_kernels(w: Workload, steps: int) -> dict:
+    """Per-kernel (launches, mean microseconds) from the library's HIP events."""
+    import torch
+    import moe_routed_expert_router_amd as moe
+    torch.cuda.synchronize()
+    moe.moe_profile_reset()
+    moe.moe_profile_enable(True)
+    for i in range(steps):
+        w.step(i)
+    torch.cuda.synchronize()
+    moe.moe_profile_enable(False)
+    stats = moe.moe_profile_read()
+    moe.moe_profile_reset()
+    return {k: (n, 1e3 * ms / n) for k, (n, ms) in stats.items() if n}
+
+
+def ffn_bytes(w: Workload, picks_per_step: list[np.ndarray]) -> dict:
+    """Algorithmic HBM bytes per launch, averaged over the steps' batches:
+    each distinct picked expert's planes read once, activations read, results
+    written (no re-reads counted)."""
+    L = w.layer
+    H, I, k = L.H, L.I, L.k
+    w13 = 2 * I * (H // 2) + 2 * I * (H // 32)
+    w2 = H * (I // 2) + H * (I // 32)
+    gu, dn, cold_bytes = [], [], []
+    for ids in picks_per_step:
+        U = len(np.unique(ids))
+        T = ids.shape[0]
+        P = T * k
+        gu.append(U * w13 + T * H * 2 + P * I * 4)           # + x read, h (hi+lo) write
+        dn.append(U * w2 + P * I * 4 + P * H * 4)            # + h read, y write
+        n_cold = sum(1 for e in np.unique(ids) if L.slot_np[e] < 0)
+        cold_bytes.append(n_cold * L.B)
+    return {"gate_up": float(np.mean(gu)), "down": float(np.mean(dn)),
+            "gather_cold": float(np.mean(cold_bytes)),
+            "unique": float(np.mean([len(np.unique(i)) for i in picks_per_step]))}
+
+
+def kernel_role(name: str) -> str | None:
+    """Which algorithmic byte count a library kernel name is measured against."""
+    if name.startswith("ffn_gate_up"):
+        return "gate_up"
+    if name.startswith("ffn_down"):
+        return "down"
+    if name == "gather_cold":
+        return "gather_cold"
+    return None
+
+
+def kernel_table(prof: dict, by: dict) -> dict:
+    out = {}
+    for k, (n, us) in sorted(prof.items()):
+        e = {"launches": n, "mean_us": round(us, 3)}
+        role = kernel_role(k)
+        if role and by.get(role):
+            e["algorithmic_bytes"] = int(by[role])
+            e["GB_per_s"] = round(by[role] / (us * 1e-6) / 1e9, 1)
+        out[k] = e
+    return out
+
+
+def role_kernel(prof: dict, role: str) -> str:
+    return next(k for k in prof if kernel_role(k) == role)
+
+
+def cpu_baseline(name: str, seconds: float) -> dict:
+    """The oracle, untuned, on the host cores: one layer for one batch of the
+    workload at a time, until about `seconds` of CPU work have run."""
+    from synth import gen
+    from oracle import layer as olayer
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    wl = gen.workload(name)
+    cal = gen.load_calibration() if wl.zipf else None
+    bias = gen.zipf_prior(wl.seed, 0, wl.n_experts, cal["alpha"]) if wl.zipf else None
+    wr = gen.router_weight(wl.seed, 0, wl.n_experts, wl.hidden)
+    n_tok, elapsed, batches = 0, 0.0, 0
+    max_batches = 64
+    while elapsed < seconds and batches < max_batches:
+        x = gen.tokens_bf16(wl.seed, 1000 + batches, wl.tokens, wl.hidden)
+        # expert bytes are input generation: regenerate outside the timed region
+        from oracle.route import route
+        ids, _, _ = route(x, wr, bias, wl.top_k)
+        blobs = {int(e): gen.expert_blob(wl.seed, 0, int(e), wl.hidden, wl.inter) for e in np.unique(ids)}
+        t0 = time.perf_counter()
+        olayer.layer_forward(x, wr, bias, lambda e: blobs[e], wl.hidden, wl.inter, wl.top_k)
+        elapsed += time.perf_counter() - t0
+        n_tok += wl.tokens
+        batches += 1
+    return {"value": n_tok / elapsed, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{batches} batches of {wl.tokens} token(s) of the {name} layer (seed {wl.seed}), "
+                      f"{elapsed:.1f} s of oracle time (route, dequant, fp32 SwiGLU FFN, combine)",
+            "host_cpus": os.cpu_count()}
+
+
+def measure(name: str, steps: int, warmup: int, reps: int, use_graph: bool, prof_steps: int):
+    import torch
+    w = Workload(name, reps)
+    try:
+        secs, steps_done, graphed = time_steps(w, steps, warmup, use_graph)
+        # picks of the pool (the graph replays exactly these batches)
+        torch.cuda.synchronize()
+        picks = [t.cpu().numpy() for t in w.ids]
+        prof = profile_kernels(w, prof_steps)
+        by = ffn_bytes(w, picks)
+        return w, secs, steps_done, graphed, prof, by
+    except Exception:
+        w.close()
+        raise
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=512)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--workload", default="decode1")
+    ap.add_argument("--reps", type=int, default=64, help="token batches in the rotation pool")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-batch8", action="store_true", help="skip the batch-8 hot/cold secondary figures")
+    a = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}, WORLD_SIZE {world}); "
+              "this layer is built and measured on a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import moe_routed_expert_router_amd as moe  # noqa: F401  (fails loudly if libmoe.so is missing)
+
+    log(f"[bench] workload {a.workload}: setup")
+    w, secs, steps, graphed, prof, by = measure(a.workload, a.steps, a.warmup, a.reps, not a.no_graph,
+                                                min(a.steps, 256))
+    wl = w.wl
+    ms_per_step = 1e3 * secs / steps
+    value = steps * wl.tokens / secs
+    log(f"[bench] {steps} steps in {secs:.4f} s ({ms_per_step * 1e3:.1f} us/step), graph={graphed}")
+    kernels = kernel_table(prof, by)
+    for k, e in kernels.items():
+        log(f"[bench]   {k:24s} {e['mean_us']:9.2f} us" + (f"  {e['GB_per_s']:8.1f} GB/s" if "GB_per_s" in e else ""))
+    dom = role_kernel(prof, "gate_up")
+    dn = role_kernel(prof, "down")
+    dom_us = prof[dom][1]
+    achieved = by["gate_up"] / (dom_us * 1e-6) / 1e9
+    traffic = read_traffic(dom, a.workload)
+    ffn_us = dom_us + prof[dn][1] + prof.get("ffn_combine", (0, 0.0))[1]
+    ffn_gbs = (by["gate_up"] + by["down"]) / (ffn_us * 1e-6) / 1e9
+    w.close()
+    del w
+    torch.cuda.empty_cache()
+
+    extra = {}
+    if not a.no_batch8 and a.workload == "decode1":
+        log("[bench] secondary: hotcold8 (batch 8, 255 hot / 129 cold)")
+        w8, s8, st8, g8, p8, b8 = measure("hotcold8", 128, 8, 16, not a.no_graph, 64)
+        k8 = kernel_table(p8, b8)
+        ffn8_us = p8[role_kernel(p8, "gate_up")][1] + p8[role_kernel(p8, "down")][1] + \
+            p8.get("ffn_combine", (0, 0.0))[1]
+        entry = {"tokens_per_s": round(st8 * 8 / s8, 1), "ms_per_step": round(1e3 * s8 / st8, 4),
+                 "graph": g8, "mean_distinct_experts": round(b8["unique"], 2),
+                 "ffn_hbm_GB_per_s": round((b8["gate_up"] + b8["down"]) / (ffn8_us * 1e-6) / 1e9, 1),
+                 "kernels": k8}
+        if "gather_cold" in p8 and b8["gather_cold"] > 0:
+            entry["gather_link_GB_per_s"] = round(b8["gather_cold"] / (p8["gather_cold"][1] * 1e-6) / 1e9, 2)
+            entry["gather_bytes_per_step"] = int(b8["gather_cold"])
+        extra["batch8_hotcold"] = entry
+        w8.close()
+        del w8
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        cpu = cpu_baseline(a.workload, a.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": a.workload, "hidden": wl.hidden, "inter": wl.inter, "n_experts": wl.n_experts,
+                   "top_k": wl.top_k, "tokens_per_step": wl.tokens, "layers": 1,
+                   "resident": "all experts in HBM" if wl.n_hot is None else f"{wl.n_hot} hot / {wl.n_cold} cold",
+                   "weights": "MXFP4 (e2m1 + e8m0/32)", "accumulate": "fp32", "graph": graphed,
+                   "token_batches_rotated": a.reps},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "bytes_per_launch": int(by["gate_up"]), "mean_launch_us": round(dom_us, 3)},
+        "ffn": {"kernels": [dom, dn], "us": round(ffn_us, 3), "hbm_GB_per_s": round(ffn_gbs, 1),
+                "frac": round(ffn_gbs / HBM_PEAK_GBS, 4)},
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    out.update(extra)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -136,7 +136,7 @@ moe_status moe_residency_check(const moe_shape *s, const int32_t *slot_host,
 moe_status moe_host_alloc(size_t bytes, int32_t flags, void **host_ptr, void **device_ptr);
 moe_status moe_host_free(void *host_ptr);
 
-/* Router (a1-a2): logits z[t,e] = sum_h x[t,h]*Wr[e,h] + bias[e] in fp32, then
+/* Router: logits z[t,e] = sum_h x[t,h]*Wr[e,h] + bias[e] in fp32, then
  * per token the k largest logits (ties to the lower expert index), listed by
  * decreasing weight, with softmax weights renormalised over the k picks
  * (renormalize != 0) or plain softmax probabilities over all E
@@ -149,7 +149,7 @@ moe_status moe_route(const moe_shape *s, int32_t n_tokens, const uint16_t *x,
                      int32_t *topk_ids, float *topk_w, float *logits_out,
                      void *ws, size_t ws_bytes, void *stream);
 
-/* Pick set (a3): for the (token, pick) pairs in topk_ids, writes
+/* Pick set: for the (token, pick) pairs in topk_ids, writes
  *   counts_out [E] int32: number of pairs routed to each expert, and
  *   cold_out [E+1] int32: cold_out[0] = number m of distinct picked experts
  *   whose slot is cold, cold_out[1..m] = those experts in increasing order.
@@ -159,7 +159,7 @@ moe_status moe_pick_set(const moe_shape *s, int32_t n_tokens, const int32_t *top
                         int32_t *counts_out, int32_t *cold_out,
                         void *ws, size_t ws_bytes, void *stream);
 
-/* Cold gather (a4): every distinct picked expert e with slot[e] < 0 is
+/* Cold gather: every distinct picked expert e with slot[e] < 0 is
  * copied whole, once, from host_cold + c*B to scratch + c*B (c = -slot[e]-1),
  * by a kernel that reads the pinned host memory directly; unpicked slots are
  * not touched.  No host round trip decides what is copied.  With
@@ -167,7 +167,7 @@ moe_status moe_pick_set(const moe_shape *s, int32_t n_tokens, const int32_t *top
 moe_status moe_gather_cold(const moe_shape *s, int32_t n_tokens, const int32_t *topk_ids,
                            const moe_residency *r, void *ws, size_t ws_bytes, void *stream);
 
-/* Grouped expert FFN and combine (a5-a8): for every pair (t, j) with
+/* Grouped expert FFN and combine: for every pair (t, j) with
  * e = topk_ids[t][j], y = W2_e (silu(W1_e x_t) * (W3_e x_t)) with fp32
  * accumulation, and out[t] = sum_j topk_w[t][j] * y_(t,j) added in j order
  * (no float atomics: the result does not depend on where experts live).
@@ -179,7 +179,7 @@ moe_status moe_expert_ffn(const moe_shape *s, int32_t n_tokens, const uint16_t *
                           const moe_residency *r, int32_t out_dtype, void *out,
                           void *ws, size_t ws_bytes, void *stream);
 
-/* The whole layer (a1-a8): moe_route, then the pick set, the cold gather
+/* The whole layer: moe_route, then the pick set, the cold gather
  * (skipped when r->n_cold == 0) and the grouped FFN with the combine, all on
  * `stream`.  topk_ids / topk_w receive the routing. */
 moe_status moe_layer_forward(const moe_shape *s, int32_t n_tokens, const uint16_t *x,
@@ -187,6 +187,18 @@ moe_status moe_layer_forward(const moe_shape *s, int32_t n_tokens, const uint16_
                              const moe_residency *r, int32_t *topk_ids, float *topk_w,
                              int32_t out_dtype, void *out,
                              void *ws, size_t ws_bytes, void *stream);
+
+/* Per-kernel timing, a tracing aid (off by default).  While enabled, each
+ * kernel the library enqueues carries a start/stop HIP event pair stamped by
+ * its own dispatch, so the times are kernel execution times.
+ * moe_profile_read(i, ...) waits for the recorded events, folds them
+ * into per-kernel totals and returns kernel i's name (static until the next
+ * reset), launch count and summed milliseconds; MOE_ERR_INVALID_ARG past the
+ * last kernel.  Not meant for use under graph capture.  moe_profile_reset()
+ * clears the totals. */
+moe_status moe_profile_enable(int32_t on);
+moe_status moe_profile_reset(void);
+moe_status moe_profile_read(int32_t index, const char **name, int64_t *count, double *total_ms);
 
 #ifdef __cplusplus
 }

@@ -2,7 +2,7 @@
 
 The computation lives in libmoe.so (hand-written HIP for gfx950 behind the C
 ABI of include/moe.h); this package only loads it and marshals arguments.
-Build it with ``python -m moe_routed_expert_router_amd.build``.
+Build it with ``python moe_routed_expert_router_amd/build.py``.
 """
 from ._lib import (  # noqa: F401
     EXPORTS, LIB_PATH, MoeError, MoeResidency, MoeShape, lib, residency, shape,
@@ -12,4 +12,5 @@ from ._lib import (  # noqa: F401
     moe_status_string, moe_last_error, moe_shape_check, moe_expert_bytes, moe_workspace_bytes,
     moe_residency_check, moe_host_alloc, moe_host_free, moe_route, moe_pick_set,
     moe_gather_cold, moe_expert_ffn, moe_layer_forward,
+    moe_profile_enable, moe_profile_reset, moe_profile_read,
 )

@@ -19,6 +19,7 @@ EXPORTS = (
     "moe_status_string", "moe_last_error", "moe_shape_check", "moe_expert_bytes",
     "moe_workspace_bytes", "moe_residency_check", "moe_host_alloc", "moe_host_free",
     "moe_route", "moe_pick_set", "moe_gather_cold", "moe_expert_ffn", "moe_layer_forward",
+    "moe_profile_enable", "moe_profile_reset", "moe_profile_read",
 )
 
 MOE_OK = 0
@@ -49,7 +50,7 @@ class MoeResidency(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run python -m moe_routed_expert_router_amd.build")
+        raise ImportError(f"{LIB_PATH} is not built; run python moe_routed_expert_router_amd/build.py")
     lib = ctypes.CDLL(LIB_PATH)
     P = c_void_p
     sig = {
@@ -68,6 +69,10 @@ def _load():
                                      P, P, c_size_t, P]),
         "moe_layer_forward": (c_int32, [POINTER(MoeShape), c_int32, P, P, P, c_int32,
                                         POINTER(MoeResidency), P, P, c_int32, P, P, c_size_t, P]),
+        "moe_profile_enable": (c_int32, [c_int32]),
+        "moe_profile_reset": (c_int32, []),
+        "moe_profile_read": (c_int32, [c_int32, POINTER(c_char_p), POINTER(ctypes.c_int64),
+                                       POINTER(ctypes.c_double)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -193,3 +198,23 @@ def moe_layer_forward(s: MoeShape, x, w_router, bias, renormalize: bool, r: MoeR
     _check(lib.moe_layer_forward(ctypes.byref(s), T, _ptr(x), _ptr(w_router), _ptr(bias), int(bool(renormalize)),
                                  ctypes.byref(r), _ptr(topk_ids), _ptr(topk_w), _out_dtype(out), _ptr(out),
                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_profile_enable(on: bool) -> None:
+    _check(lib.moe_profile_enable(1 if on else 0))
+
+
+def moe_profile_reset() -> None:
+    _check(lib.moe_profile_reset())
+
+
+def moe_profile_read() -> dict:
+    """{kernel name: (launch count, total milliseconds)} of the recorded launches."""
+    out = {}
+    i = 0
+    while True:
+        name, cnt, ms = c_char_p(), ctypes.c_int64(), ctypes.c_double()
+        if lib.moe_profile_read(i, ctypes.byref(name), ctypes.byref(cnt), ctypes.byref(ms)) != MOE_OK:
+            return out
+        out[name.value.decode()] = (cnt.value, ms.value)
+        i += 1

@@ -1,6 +1,8 @@
 """Build libmoe.so (the C-ABI HIP library) in-tree for gfx950.
 
-    python -m moe_routed_expert_router_amd.build [--jobs N]
+    python moe_routed_expert_router_amd/build.py [--jobs N]
+
+(run as a script: importing the package would load the library it builds)
 
 Every .hip source under csrc/ is compiled with hipcc for gfx950 only and
 linked into moe_routed_expert_router_amd/libmoe.so.  Packed fp32 vector ops

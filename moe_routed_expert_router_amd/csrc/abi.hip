@@ -343,10 +343,15 @@ moe_status moe_layer_forward(const moe_shape *s, int32_t T, const uint16_t *x, c
     char *w = static_cast<char *>(ws);
     hipStream_t st = static_cast<hipStream_t>(stream);
     float *z = reinterpret_cast<float *>(w + L.logits);
-    TRY(hip_status(moe::launch_route_logits(x, w_router, bias, T, H, E, z, st), "router logits launch"));
-    TRY(hip_status(moe::launch_topk(z, T, E, k, renormalize != 0, topk_ids, topk_w, st), "top-k launch"));
     const moe::GroupArgs g = group_args(s, T, topk_ids, r);
-    TRY(hip_status(moe::launch_group(g, w, L, st), "pick-set launch"));
+    TRY(hip_status(moe::launch_route_logits(x, w_router, bias, T, H, E, z, st), "router logits launch"));
+    if (T <= moe::kSmallRouteTokens) {
+        TRY(hip_status(moe::launch_select_group_small(z, T, k, renormalize != 0, topk_ids, topk_w, g, w, L, st),
+                       "select-and-group launch"));
+    } else {
+        TRY(hip_status(moe::launch_topk(z, T, E, k, renormalize != 0, topk_ids, topk_w, st), "top-k launch"));
+        TRY(hip_status(moe::launch_group(g, w, L, st), "pick-set launch"));
+    }
     if (r->n_cold > 0)
         TRY(hip_status(moe::launch_gather(r->host_cold, r->scratch, g.blob_bytes, r->slot, w, L, st),
                        "gather launch"));

@@ -39,6 +39,7 @@ struct BlobLayout {
 // ------------------------------- workspace ---------------------------------
 // Regions of the caller's workspace for T tokens (all 256-byte aligned).
 struct WsLayout {
+    size_t sync;       // int32 [kSyncWords]: FFN completion counters (zeroed by the grouping)
     size_t logits;     // float [T][E]
     size_t status;     // int32 [16]: [0] invalid-pair count, [1] bad-residency count
     size_t nuniq;      // int32 [4]: [0] distinct experts U, [1] picked-cold count
@@ -56,7 +57,8 @@ struct WsLayout {
     size_t total;
     int nchunks;
 
-    static constexpr int kChunk = 256;   // pairs per grouping chunk
+    static constexpr int kChunk = 256;      // pairs per grouping chunk
+    static constexpr int kSyncWords = 4096;  // >= H/32 for H <= 65536 (+ spare)
 
     static size_t up(size_t v) { return (v + 255) & ~(size_t)255; }
     static WsLayout make(int H, int I, int E, int k, int T) {
@@ -65,6 +67,7 @@ struct WsLayout {
         w.nchunks = (int)((P + kChunk - 1) / kChunk);
         size_t o = 0;
         auto take = [&](size_t bytes) { size_t r = o; o += up(bytes > 0 ? bytes : 1); return r; };
+        w.sync = take((size_t)kSyncWords * 4);
         w.logits = take((size_t)T * E * 4);
         w.status = take(16 * 4);
         w.nuniq = take(4 * 4);
@@ -86,6 +89,7 @@ struct WsLayout {
 
 // Device view of the grouped pick set, resolved from a workspace base.
 struct GroupView {
+    int32_t *sync;          // completion counters, zero on entry to the FFN
     const int32_t *nuniq;   // [0] U, [1] picked-cold count
     const int32_t *uniq;
     const int32_t *ucnt;
@@ -94,6 +98,39 @@ struct GroupView {
     const int32_t *plist;
     const int32_t *cold;
 };
+
+// Mutable view of the grouping outputs, for the kernels that write them.
+struct GroupOut {
+    int32_t *sync, *status, *counts, *nuniq, *uniq, *ucnt, *uoff, *cold, *plist;
+    uint64_t *uptr;
+    static GroupOut at(char *ws, const WsLayout &L) {
+        GroupOut o;
+        o.sync = reinterpret_cast<int32_t *>(ws + L.sync);
+        o.status = reinterpret_cast<int32_t *>(ws + L.status);
+        o.counts = reinterpret_cast<int32_t *>(ws + L.counts);
+        o.nuniq = reinterpret_cast<int32_t *>(ws + L.nuniq);
+        o.uniq = reinterpret_cast<int32_t *>(ws + L.uniq);
+        o.ucnt = reinterpret_cast<int32_t *>(ws + L.ucnt);
+        o.uoff = reinterpret_cast<int32_t *>(ws + L.uoff);
+        o.cold = reinterpret_cast<int32_t *>(ws + L.cold);
+        o.plist = reinterpret_cast<int32_t *>(ws + L.plist);
+        o.uptr = reinterpret_cast<uint64_t *>(ws + L.uptr);
+        return o;
+    }
+};
+
+inline GroupView group_view(char *ws, const WsLayout &L) {
+    GroupView v;
+    v.sync = reinterpret_cast<int32_t *>(ws + L.sync);
+    v.nuniq = reinterpret_cast<const int32_t *>(ws + L.nuniq);
+    v.uniq = reinterpret_cast<const int32_t *>(ws + L.uniq);
+    v.ucnt = reinterpret_cast<const int32_t *>(ws + L.ucnt);
+    v.uoff = reinterpret_cast<const int32_t *>(ws + L.uoff);
+    v.uptr = reinterpret_cast<const uint64_t *>(ws + L.uptr);
+    v.plist = reinterpret_cast<const int32_t *>(ws + L.plist);
+    v.cold = reinterpret_cast<const int32_t *>(ws + L.cold);
+    return v;
+}
 
 // ------------------------------ numerics -----------------------------------
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
@@ -125,6 +162,25 @@ __device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t w, float scale) {
     r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
     r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
     return r;
+}
+
+// Load through the global address space (blob addresses come from an integer
+// table, so the compiler would otherwise emit generic flat loads).
+template <typename T>
+__device__ __forceinline__ T gload(const void *p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    typedef const __attribute__((address_space(1))) T gT;
+    return *(gT *)(p);   // an address-space cast needs the C form
+#else
+    return *reinterpret_cast<const T *>(p);   // host pass: never executed
+#endif
+}
+
+// 16 bytes through the global address space (a native vector, so no copy
+// constructor takes a generic reference on the way).
+__device__ __forceinline__ uint4 gload16(const void *p) {
+    const u32x4 v = gload<u32x4>(p);
+    return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {

@@ -1,51 +1,223 @@
-// Grouped SwiGLU expert FFN and weighted combine (a5-a8), decode path.
+// Grouped SwiGLU expert FFN and weighted combine.
 //
 // The gracetier write-up (section 1) runs every picked expert "in a single
-// call, as if they had been in HBM all along": here a blob-address table from
-// the grouping points each distinct expert at its HBM home or its scratch
-// slot, and the kernels never look at residency again, so an all-hot run and a
+// call, as if they had been in HBM all along": a blob-address table from the
+// grouping points each distinct expert at its HBM home or its scratch slot,
+// and the kernels never look at residency again, so an all-hot run and a
 // mixed hot/cold run execute identical instructions on identical bytes.
 //
 // At decode an expert sees a handful of tokens and the work is a bandwidth-
 // bound grouped GEMV over MXFP4 weights.  It still runs on the matrix cores:
-// a wave owns 16 weight rows and streams them with 128-bit loads (per 128-
-// element K step a lane loads one 16-byte run of 32 codes, i.e. exactly one
-// MX block, plus the dword holding that row's four block scales), turns codes
-// into exact bf16 with the gfx950 scaled fp4 converts, and feeds 16x16x32 bf16
-// MFMAs whose other operand holds up to 16 tokens.  The K order inside a step
-// is permuted identically in both operands (lane group g takes block 4s+g), so
-// every MFMA is an exact partial dot product.  Compared with a VALU dot, the
-// converts are the only per-element vector work (a fifth of the issue slots
-// at the HBM rate), and 1 to 16 tokens per expert cost the same.
+// a wave owns 16 weight rows; per 128-element K step a lane loads one 16-byte
+// run of 32 codes (exactly one MX block) and that row's block scale, turns the
+// codes into exact bf16 with the gfx950 scaled fp4 converts, and feeds 16x16x32
+// bf16 MFMAs whose other operand holds up to 16 tokens.  The K order inside a
+// step is permuted identically in both operands (lane group g takes block
+// 4s+g), so every MFMA is an exact partial dot product.  The converts are the
+// only per-element vector work (about a fifth of the issue slots at the HBM
+// rate), and 1 to 16 tokens per expert cost the same.
 //
-//   gate/up: A = gate and up rows (two accumulators share the token operand);
-//            epilogue h = silu(g) * u, stored as bf16 hi + lo parts (h - hi
-//            rounded again), which carry ~16 significant bits into the down
-//            projection's bf16 MFMAs.
-//   down:    A = w2 rows, B = h hi and h lo (two MFMAs per K slice), output
-//            y[pair][row] in fp32.
-//   combine: out[t] = sum_j w[t,j] * y[t*k+j] in j order, no atomics.
+// Decode kernels (T <= 32), one 512-thread block per (row tile, expert):
+//   gate/up: 8 waves = {gate, up} x 4 K slices; each wave issues all of its
+//            slice's weight loads at once (memory-level parallelism comes
+//            from many small independent waves, not deep per-wave pipelines);
+//            tokens are staged once per block in LDS; the slice partials are
+//            added in a fixed order in LDS; h = silu(g) * u is stored as bf16
+//            hi + lo parts (h - hi rounded again), ~16 significant bits.
+//   down:    8 waves = 2 row tiles x 4 K slices over a 32-row block, B = h hi
+//            and h lo (two MFMAs per K slice), y[pair][row] in fp32.
+// General kernels (any T): one wave per 16 rows.
+// Both end with the combine kernel: out[t] = sum_j w[t,j] * y[t*k+j] in j
+// order, no float atomics.  (Folding the combine into the down kernel through
+// a last-arriver counter needs an agent-scope release per block, which on
+// this GPU writes the XCD's L2 back each time and costs more than the launch
+// it saves.)
 #include "kernels.hpp"
 
 namespace moe {
 
 namespace {
 
-GroupView group_view(const char *ws, const WsLayout &L) {
-    GroupView v;
-    v.nuniq = reinterpret_cast<const int32_t *>(ws + L.nuniq);
-    v.uniq = reinterpret_cast<const int32_t *>(ws + L.uniq);
-    v.ucnt = reinterpret_cast<const int32_t *>(ws + L.ucnt);
-    v.uoff = reinterpret_cast<const int32_t *>(ws + L.uoff);
-    v.uptr = reinterpret_cast<const uint64_t *>(ws + L.uptr);
-    v.plist = reinterpret_cast<const int32_t *>(ws + L.plist);
-    v.cold = reinterpret_cast<const int32_t *>(ws + L.cold);
-    return v;
+__device__ __forceinline__ uint2 pack_bf16x4(const uint32_t v[4]) {
+    return make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
+}
+
+__device__ __forceinline__ void split_store_h(const f32x4 &g, const f32x4 &u, uint16_t *hi_dst, uint16_t *lo_dst) {
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float h = silu(g[i]) * u[i];
+        hi[i] = f32_to_bf16_bits(h);
+        lo[i] = f32_to_bf16_bits(h - __uint_as_float(hi[i] << 16));
+    }
+    *reinterpret_cast<uint2 *>(hi_dst) = pack_bf16x4(hi);
+    *reinterpret_cast<uint2 *>(lo_dst) = pack_bf16x4(lo);
 }
 
 }  // namespace
 
-// ------------------------------- gate / up ---------------------------------
+// ============================ decode block kernels ==========================
+constexpr int kStageBytes = 49152;   // LDS budget for staged tokens / h rows
+
+// grid (I/16, max distinct experts), 128 * slices threads; LDS: NT rows of x
+// and the per-wave partial sums.
+template <int SPW>
+__global__ __launch_bounds__(512) void ffn_gate_up_blk(const uint16_t *__restrict__ x, int H, int I, int k,
+                                                       int NT, GroupView gv, uint16_t *__restrict__ hhi,
+                                                       uint16_t *__restrict__ hlo) {
+    extern __shared__ __align__(16) char smem[];
+    const int u = blockIdx.y;
+    if (u >= gv.nuniq[0]) return;
+    const uint8_t *base = reinterpret_cast<const uint8_t *>(gv.uptr[u]);
+    if (base == nullptr) return;
+    const int n = gv.ucnt[u], q0 = gv.uoff[u];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
+    const int nw = blockDim.x >> 6;
+    const int role = wave & 1, slice = wave >> 1;   // role 0: gate rows, 1: up rows
+    const int rt = blockIdx.x;
+    const BlobLayout L = BlobLayout::make(H, I);
+    const size_t row = (size_t)role * I + (size_t)rt * 16 + r;
+    const uint8_t *qp = base + L.w13_codes + row * (H / 2) + (size_t)slice * SPW * 64 + 16 * g;
+    const uint8_t *sp = base + L.w13_scales + row * (H / 32) + (size_t)slice * SPW * 4;
+
+    // every weight load of this wave's slice, in flight together
+    uint4 q[SPW];
+    uint32_t sc[SPW];
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) q[i] = gload16(qp + (size_t)i * 64);
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) sc[i] = gload<uint32_t>(sp + 4 * i);
+
+    // LDS rows in 16-byte units, padded by one unit: conflict-free token reads
+    const int stride = H / 8 + 1;
+    uint4 *xs = reinterpret_cast<uint4 *>(smem);
+    f32x4 *red = reinterpret_cast<f32x4 *>(smem + (size_t)NT * stride * 16);
+    for (int tb = 0; tb < n; tb += NT) {
+        const int nt = (n - tb) < NT ? (n - tb) : NT;
+        __syncthreads();
+        for (int c = 0; c < nt; ++c) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)(gv.plist[q0 + tb + c] / k) * H);
+            for (int j = tid; j < H / 8; j += blockDim.x) xs[c * stride + j] = src[j];
+        }
+        __syncthreads();
+        // MFMA output columns are independent, so a lane whose token column is
+        // empty reads row 0 and its column is never stored: no masked reads
+        const bool tv = r < nt;   // this lane's token column
+        const uint4 *xr = xs + (tv ? r : 0) * stride + slice * SPW * 16 + 4 * g;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            float s = e8m0_to_f32((sc[i] >> (8 * g)) & 0xffu);
+            // converted weights are loop-invariant across token passes; keep
+            // the converts at their step instead of holding 4x the registers
+            asm volatile("" : "+v"(s));
+            const uint32_t w4[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                acc = mfma16x16x32(fp4x8_to_bf16x8(w4[m], s), as_bf16x8(xr[i * 16 + m]), acc);
+            }
+            // one step's operands live at a time (keeps three blocks per CU)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        red[wave * 64 + lane] = acc;
+        __syncthreads();
+        if (wave == 0) {
+            f32x4 gs = red[lane], us = red[64 + lane];
+            for (int w = 2; w < nw; w += 2) {   // slices in a fixed order
+                gs += red[w * 64 + lane];
+                us += red[(w + 1) * 64 + lane];
+            }
+            if (tv) {
+                const size_t off = (size_t)(q0 + tb + r) * I + (size_t)rt * 16 + 4 * g;
+                split_store_h(gs, us, hhi + off, hlo + off);
+            }
+        }
+    }
+}
+
+// grid (H/32, max distinct experts), 128 * slices threads; LDS: NT rows of h
+// hi and lo and the per-wave partial sums.
+template <int SPW>
+__global__ __launch_bounds__(512) void ffn_down_blk(int H, int I, int NT, GroupView gv,
+                                                    const uint16_t *__restrict__ hhi,
+                                                    const uint16_t *__restrict__ hlo, float *__restrict__ y) {
+    extern __shared__ __align__(16) char smem[];
+    const int u = blockIdx.y;
+    if (u >= gv.nuniq[0]) return;
+    const uint8_t *base = reinterpret_cast<const uint8_t *>(gv.uptr[u]);
+    const int n = gv.ucnt[u], q0 = gv.uoff[u];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
+    const int nw = blockDim.x >> 6;
+    const int rt = wave & 1, slice = wave >> 1;   // 2 row tiles x slices
+    const int rb = blockIdx.x;
+    const int row0 = rb * 32;
+    const BlobLayout L = BlobLayout::make(H, I);
+
+    if (base == nullptr) {   // unusable residency entry: its pairs contribute zero
+        for (int i = tid; i < n * 8; i += blockDim.x) {
+            const int p = gv.plist[q0 + i / 8];
+            reinterpret_cast<float4 *>(y + (size_t)p * H + row0)[i % 8] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    } else {
+        const size_t row = (size_t)row0 + rt * 16 + r;
+        const uint8_t *qp = base + L.w2_codes + row * (I / 2) + (size_t)slice * SPW * 64 + 16 * g;
+        const uint8_t *sp = base + L.w2_scales + row * (I / 32) + (size_t)slice * SPW * 4;
+        uint4 q[SPW];
+        uint32_t sc[SPW];
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) q[i] = gload16(qp + (size_t)i * 64);
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) sc[i] = gload<uint32_t>(sp + 4 * i);
+
+        const int stride = I / 8 + 1;   // 16-byte units, padded
+        uint4 *hs = reinterpret_cast<uint4 *>(smem);
+        uint4 *ls = hs + (size_t)NT * stride;
+        f32x4 *red = reinterpret_cast<f32x4 *>(smem + (size_t)2 * NT * stride * 16);
+        for (int tb = 0; tb < n; tb += NT) {
+            const int nt = (n - tb) < NT ? (n - tb) : NT;
+            __syncthreads();
+            for (int c = 0; c < nt; ++c) {
+                const uint4 *sh = reinterpret_cast<const uint4 *>(hhi + (size_t)(q0 + tb + c) * I);
+                const uint4 *sl = reinterpret_cast<const uint4 *>(hlo + (size_t)(q0 + tb + c) * I);
+                for (int j = tid; j < I / 8; j += blockDim.x) {
+                    hs[c * stride + j] = sh[j];
+                    ls[c * stride + j] = sl[j];
+                }
+            }
+            __syncthreads();
+            const bool tv = r < nt;
+            const int lo = (tv ? r : 0) * stride + slice * SPW * 16 + 4 * g;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < SPW; ++i) {
+                float s = e8m0_to_f32((sc[i] >> (8 * g)) & 0xffu);
+                asm volatile("" : "+v"(s));   // keep the converts at their step
+                const uint32_t w4[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const bf16x8 a = fp4x8_to_bf16x8(w4[m], s);
+                    acc = mfma16x16x32(a, as_bf16x8(hs[lo + i * 16 + m]), acc);
+                    acc = mfma16x16x32(a, as_bf16x8(ls[lo + i * 16 + m]), acc);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            red[wave * 64 + lane] = acc;
+            __syncthreads();
+            if (wave < 2) {   // wave rt adds its row tile's slices in a fixed order
+                f32x4 s = red[wave * 64 + lane];
+                for (int w2 = wave + 2; w2 < nw; w2 += 2) s += red[w2 * 64 + lane];
+                if (tv) {
+                    const int p = gv.plist[q0 + tb + r];
+                    *reinterpret_cast<float4 *>(y + (size_t)p * H + row0 + wave * 16 + 4 * g) =
+                        make_float4(s[0], s[1], s[2], s[3]);
+                }
+            }
+        }
+    }
+
+}
+
+// ========================= general one-wave kernels =========================
 template <int D>
 struct GateUpStage {
     uint4 gq[D], uq[D];      // 32 codes of a gate row / an up row per step
@@ -90,9 +262,9 @@ __device__ __forceinline__ void gate_up_compute(const GateUpStage<D> &st, int g,
 
 // grid (I/16, max distinct experts), one wave per block.
 template <int D>
-__global__ __launch_bounds__(64) void ffn_gate_up(const uint16_t *__restrict__ x, int H, int I, int k,
-                                                  GroupView gv, uint16_t *__restrict__ hhi,
-                                                  uint16_t *__restrict__ hlo) {
+__global__ __launch_bounds__(64) void ffn_gate_up_wave(const uint16_t *__restrict__ x, int H, int I, int k,
+                                                       GroupView gv, uint16_t *__restrict__ hhi,
+                                                       uint16_t *__restrict__ hlo) {
     const int u = blockIdx.y;
     if (u >= gv.nuniq[0]) return;
     const uint8_t *base = reinterpret_cast<const uint8_t *>(gv.uptr[u]);
@@ -123,21 +295,12 @@ __global__ __launch_bounds__(64) void ffn_gate_up(const uint16_t *__restrict__ x
         }
         // lane (r, g) holds rows 4g..4g+3 of the tile for token column r
         if (tv) {
-            uint32_t hi[4], lo[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float h = silu(ag[i]) * au[i];
-                hi[i] = f32_to_bf16_bits(h);
-                lo[i] = f32_to_bf16_bits(h - __uint_as_float(hi[i] << 16));
-            }
             const size_t off = (size_t)(q0 + tb + r) * I + (size_t)blockIdx.x * 16 + 4 * g;
-            *reinterpret_cast<uint2 *>(hhi + off) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
-            *reinterpret_cast<uint2 *>(hlo + off) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+            split_store_h(ag, au, hhi + off, hlo + off);
         }
     }
 }
 
-// --------------------------------- down ------------------------------------
 template <int D>
 struct DownStage {
     uint4 wq[D];
@@ -179,8 +342,8 @@ __device__ __forceinline__ void down_compute(const DownStage<D> &st, int g, f32x
 
 // grid (H/16, max distinct experts), one wave per block.
 template <int D>
-__global__ __launch_bounds__(64) void ffn_down(int H, int I, GroupView gv, const uint16_t *__restrict__ hhi,
-                                               const uint16_t *__restrict__ hlo, float *__restrict__ y) {
+__global__ __launch_bounds__(64) void ffn_down_wave(int H, int I, GroupView gv, const uint16_t *__restrict__ hhi,
+                                                    const uint16_t *__restrict__ hlo, float *__restrict__ y) {
     const int u = blockIdx.y;
     if (u >= gv.nuniq[0]) return;
     const uint8_t *base = reinterpret_cast<const uint8_t *>(gv.uptr[u]);
@@ -220,7 +383,6 @@ __global__ __launch_bounds__(64) void ffn_down(int H, int I, GroupView gv, const
     }
 }
 
-// -------------------------------- combine ----------------------------------
 __global__ __launch_bounds__(256) void ffn_combine(const float *__restrict__ y, const int32_t *__restrict__ ids,
                                                    const float *__restrict__ w, int T, int H, int E, int k,
                                                    int out_bf16, void *__restrict__ out) {
@@ -239,14 +401,79 @@ __global__ __launch_bounds__(256) void ffn_combine(const float *__restrict__ y, 
             acc.w += wj * v.w;
         }
         if (out_bf16) {
-            const uint32_t b0 = f32_to_bf16_bits(acc.x), b1 = f32_to_bf16_bits(acc.y);
-            const uint32_t b2 = f32_to_bf16_bits(acc.z), b3 = f32_to_bf16_bits(acc.w);
-            reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + (size_t)t * H)[c4] =
-                make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+            const uint32_t b[4] = {f32_to_bf16_bits(acc.x), f32_to_bf16_bits(acc.y), f32_to_bf16_bits(acc.z),
+                                   f32_to_bf16_bits(acc.w)};
+            reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + (size_t)t * H)[c4] = pack_bf16x4(b);
         } else {
             reinterpret_cast<float4 *>(static_cast<float *>(out) + (size_t)t * H)[c4] = acc;
         }
     }
+}
+
+// ================================ launchers =================================
+namespace {
+
+// Smallest steps-per-wave in {1,2,4,8,16} dividing `steps` with at most
+// max_slices slices; 0 if none.
+int pick_spw(int steps, int max_slices) {
+    for (int spw = 1; spw <= 16; spw *= 2)
+        if (steps % spw == 0 && steps / spw <= max_slices) return spw;
+    return 0;
+}
+
+int stage_rows(int bytes_per_row) {
+    const int nt = kStageBytes / bytes_per_row;
+    return nt < 1 ? 1 : (nt > 16 ? 16 : nt);
+}
+
+template <int SPW>
+void launch_gate_up_blk(const FfnArgs &a, const GroupView &gv, uint16_t *hhi, uint16_t *hlo, int umax,
+                        hipStream_t st) {
+    const int slices = a.H / 128 / SPW;
+    const int row_bytes = (a.H / 8 + 1) * 16;
+    const int NT = stage_rows(row_bytes);
+    const size_t lds = (size_t)NT * row_bytes + (size_t)2 * slices * 64 * 16;
+    MOE_LAUNCH("ffn_gate_up_blk", ffn_gate_up_blk<SPW>, dim3(a.I / 16, umax), dim3(128 * slices), lds, st, a.x,
+               a.H, a.I, a.k, NT, gv, hhi, hlo);
+}
+
+template <int SPW>
+void launch_down_blk(const FfnArgs &a, const GroupView &gv, const uint16_t *hhi, const uint16_t *hlo, float *y,
+                     int umax, hipStream_t st) {
+    const int slices = a.I / 128 / SPW;
+    const int row_bytes = (a.I / 8 + 1) * 16;
+    const int NT = stage_rows(2 * row_bytes);
+    const size_t lds = (size_t)2 * NT * row_bytes + (size_t)2 * slices * 64 * 16;
+    MOE_LAUNCH("ffn_down_blk", ffn_down_blk<SPW>, dim3(a.H / 32, umax), dim3(128 * slices), lds, st, a.H, a.I,
+               NT, gv, hhi, hlo, y);
+}
+
+void gate_up_blk(int spw, const FfnArgs &a, const GroupView &gv, uint16_t *hhi, uint16_t *hlo, int umax,
+                 hipStream_t st) {
+    switch (spw) {
+        case 1: launch_gate_up_blk<1>(a, gv, hhi, hlo, umax, st); break;
+        case 2: launch_gate_up_blk<2>(a, gv, hhi, hlo, umax, st); break;
+        case 4: launch_gate_up_blk<4>(a, gv, hhi, hlo, umax, st); break;
+        case 8: launch_gate_up_blk<8>(a, gv, hhi, hlo, umax, st); break;
+        default: launch_gate_up_blk<16>(a, gv, hhi, hlo, umax, st); break;
+    }
+}
+
+void down_blk(int spw, const FfnArgs &a, const GroupView &gv, const uint16_t *hhi, const uint16_t *hlo, float *y,
+              int umax, hipStream_t st) {
+    switch (spw) {
+        case 1: launch_down_blk<1>(a, gv, hhi, hlo, y, umax, st); break;
+        case 2: launch_down_blk<2>(a, gv, hhi, hlo, y, umax, st); break;
+        case 4: launch_down_blk<4>(a, gv, hhi, hlo, y, umax, st); break;
+        case 8: launch_down_blk<8>(a, gv, hhi, hlo, y, umax, st); break;
+        default: launch_down_blk<16>(a, gv, hhi, hlo, y, umax, st); break;
+    }
+}
+
+}  // namespace
+
+bool ffn_block_path(int T, int H, int I) {
+    return T <= 32 && pick_spw(H / 128, 4) != 0 && pick_spw(I / 128, 4) != 0;
 }
 
 hipError_t launch_ffn(const FfnArgs &a, char *ws, const WsLayout &L, hipStream_t st) {
@@ -257,26 +484,33 @@ hipError_t launch_ffn(const FfnArgs &a, char *ws, const WsLayout &L, hipStream_t
     uint16_t *hlo = hhi + P * (size_t)a.I;
     float *y = reinterpret_cast<float *>(ws + L.ybuf);
 
-    const int sgu = a.H / 128;
-    const dim3 ggu(a.I / 16, umax);
-    if (sgu % 4 == 0)
-        hipLaunchKernelGGL(ffn_gate_up<4>, ggu, dim3(64), 0, st, a.x, a.H, a.I, a.k, gv, hhi, hlo);
-    else if (sgu % 2 == 0)
-        hipLaunchKernelGGL(ffn_gate_up<2>, ggu, dim3(64), 0, st, a.x, a.H, a.I, a.k, gv, hhi, hlo);
-    else
-        hipLaunchKernelGGL(ffn_gate_up<1>, ggu, dim3(64), 0, st, a.x, a.H, a.I, a.k, gv, hhi, hlo);
-
-    const int sd = a.I / 128;
-    const dim3 gd(a.H / 16, umax);
-    if (sd % 2 == 0)
-        hipLaunchKernelGGL(ffn_down<2>, gd, dim3(64), 0, st, a.H, a.I, gv, hhi, hlo, y);
-    else
-        hipLaunchKernelGGL(ffn_down<1>, gd, dim3(64), 0, st, a.H, a.I, gv, hhi, hlo, y);
+    if (ffn_block_path(a.T, a.H, a.I)) {
+        gate_up_blk(pick_spw(a.H / 128, 4), a, gv, hhi, hlo, umax, st);
+        down_blk(pick_spw(a.I / 128, 4), a, gv, hhi, hlo, y, umax, st);
+    } else {
+        const int sgu = a.H / 128;
+        const dim3 ggu(a.I / 16, umax);
+        if (sgu % 4 == 0)
+            MOE_LAUNCH("ffn_gate_up_wave", ffn_gate_up_wave<4>, ggu, dim3(64), 0, st, a.x, a.H, a.I, a.k, gv, hhi,
+                       hlo);
+        else if (sgu % 2 == 0)
+            MOE_LAUNCH("ffn_gate_up_wave", ffn_gate_up_wave<2>, ggu, dim3(64), 0, st, a.x, a.H, a.I, a.k, gv, hhi,
+                       hlo);
+        else
+            MOE_LAUNCH("ffn_gate_up_wave", ffn_gate_up_wave<1>, ggu, dim3(64), 0, st, a.x, a.H, a.I, a.k, gv, hhi,
+                       hlo);
+        const int sd = a.I / 128;
+        const dim3 gd(a.H / 16, umax);
+        if (sd % 2 == 0)
+            MOE_LAUNCH("ffn_down_wave", ffn_down_wave<2>, gd, dim3(64), 0, st, a.H, a.I, gv, hhi, hlo, y);
+        else
+            MOE_LAUNCH("ffn_down_wave", ffn_down_wave<1>, gd, dim3(64), 0, st, a.H, a.I, gv, hhi, hlo, y);
+    }
 
     const int n4 = a.H / 4;
     const int ty = a.T < 65535 ? a.T : 65535;
-    hipLaunchKernelGGL(ffn_combine, dim3((n4 + 255) / 256, ty), dim3(256), 0, st, y, a.ids, a.w, a.T, a.H,
-                       a.E, a.k, a.out_bf16, a.out);
+    MOE_LAUNCH("ffn_combine", ffn_combine, dim3((n4 + 255) / 256, ty), dim3(256), 0, st, y, a.ids, a.w, a.T, a.H,
+               a.E, a.k, a.out_bf16, a.out);
     return hipGetLastError();
 }
 

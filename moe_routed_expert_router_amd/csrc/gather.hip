@@ -1,4 +1,4 @@
-// Cold gather (a4): copy the picked cold experts from pinned host memory into
+// Cold gather: copy the picked cold experts from pinned host memory into
 // their HBM scratch slots.  The gracetier write-up (section 1) keeps the 129
 // cold experts of a layer in pinned host memory the GPU reads directly and has
 // one small kernel per layer copy just the picked ones into their slots; its
@@ -51,7 +51,7 @@ hipError_t launch_gather(const uint8_t *host_cold, uint8_t *scratch, size_t blob
     const size_t per_iter = (size_t)kGatherThreads * kGatherUnroll;
     size_t blocks = (units + per_iter - 1) / per_iter;
     if (blocks > kGatherBlocks) blocks = kGatherBlocks;
-    hipLaunchKernelGGL(gather_cold, dim3((unsigned)blocks), dim3(kGatherThreads), 0, st, host_cold, scratch,
+    MOE_LAUNCH("gather_cold", gather_cold, dim3((unsigned)blocks), dim3(kGatherThreads), 0, st, host_cold, scratch,
                        blob_bytes, slot, reinterpret_cast<const int32_t *>(ws + L.nuniq),
                        reinterpret_cast<const int32_t *>(ws + L.cold));
     return hipGetLastError();

@@ -1,4 +1,4 @@
-// Pick set / grouping (a3): which experts the router picked, the (token, pick)
+// Pick set / grouping: which experts the router picked, the (token, pick)
 // pairs of each, and the picked cold experts.  The gracetier write-up (section
 // 1) has one small kernel look at the router's picks; here that look is these
 // three small kernels, and nothing goes back to the host.
@@ -8,6 +8,7 @@
 // expert.  One block then turns the histograms into per-expert runs (stable:
 // inside a run pairs keep increasing p), the distinct-expert list, the
 // blob-address table and the picked-cold list.  A last pass scatters pair ids.
+#include "device_util.hpp"
 #include "kernels.hpp"
 
 namespace moe {
@@ -43,35 +44,6 @@ __global__ __launch_bounds__(kChunk) void group_hist(const int32_t *__restrict__
     for (int i = tid; i <= E; i += kChunk) row[i] = cnt[i];
 }
 
-// Exclusive scan across a 1024-thread block; returns the block total in *tot.
-__device__ int block_exscan(int v, int *lds, int *tot) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int inc = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(inc, off);
-        if (lane >= off) inc += o;
-    }
-    if (lane == 63) lds[wave] = inc;
-    __syncthreads();
-    if (wave == 0) {
-        int w = (lane < 16) ? lds[lane] : 0;
-        int wi = w;
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-            const int o = __shfl_up(wi, off);
-            if (lane >= off) wi += o;
-        }
-        if (lane < 16) lds[16 + lane] = wi - w;
-        if (lane == 15) lds[32] = wi;
-    }
-    __syncthreads();
-    const int r = lds[16 + wave] + inc - v;
-    *tot = lds[32];
-    __syncthreads();
-    return r;
-}
-
 __global__ __launch_bounds__(1024) void group_scan(int nchunks, int E, const int32_t *__restrict__ slot,
                                                    int n_hot, int n_cold, const uint8_t *hot_base,
                                                    const uint8_t *scratch, size_t blob_bytes,
@@ -79,9 +51,10 @@ __global__ __launch_bounds__(1024) void group_scan(int nchunks, int E, const int
                                                    int32_t *__restrict__ nuniq, int32_t *__restrict__ uniq,
                                                    int32_t *__restrict__ ucnt, int32_t *__restrict__ uoff,
                                                    uint64_t *__restrict__ uptr, int32_t *__restrict__ cold,
-                                                   int32_t *__restrict__ status) {
+                                                   int32_t *__restrict__ status, int32_t *__restrict__ sync) {
     __shared__ int lds[40];
     const int e = threadIdx.x;
+    for (int i = e; i < WsLayout::kSyncWords; i += 1024) sync[i] = 0;
     const int stride = E + 1;
     int total = 0;
     if (e < E) {
@@ -94,35 +67,26 @@ __global__ __launch_bounds__(1024) void group_scan(int nchunks, int E, const int
     const bool is_exp = e < E;
     const int cnt = is_exp ? total : 0;
     int ntot;
-    const int off = block_exscan(cnt, lds, &ntot);
+    const int off = block_exscan1024(cnt, lds, &ntot);
     // residency: never point outside [0, n_hot) / [0, n_cold)
-    int s = 0;
-    bool ok = false;
-    if (is_exp) {
-        s = slot[e];
-        ok = (s >= 0) ? (s < n_hot && hot_base != nullptr)
-                      : (-s - 1 < n_cold && scratch != nullptr);
-    }
+    bool ok = false, in_cold = false;
+    const uint64_t addr =
+        is_exp ? expert_address(slot[e], n_hot, n_cold, hot_base, scratch, blob_bytes, &ok, &in_cold) : 0;
     const bool picked = cnt > 0;
     int nu;
-    const int ui = block_exscan(picked ? 1 : 0, lds, &nu);
-    const bool is_cold = picked && ok && s < 0;
+    const int ui = block_exscan1024(picked ? 1 : 0, lds, &nu);
+    const bool is_cold = picked && ok && in_cold;
     int nc;
-    const int ci = block_exscan(is_cold ? 1 : 0, lds, &nc);
+    const int ci = block_exscan1024(is_cold ? 1 : 0, lds, &nc);
     int nbad;
-    block_exscan((picked && !ok) ? 1 : 0, lds, &nbad);
+    block_exscan1024((picked && !ok) ? 1 : 0, lds, &nbad);
     if (is_exp) {
         counts[e] = cnt;
         if (picked) {
             uniq[ui] = e;
             ucnt[ui] = cnt;
             uoff[ui] = off;
-            uint64_t a = 0;
-            if (ok) {
-                a = (s >= 0) ? (uint64_t)(hot_base + (size_t)s * blob_bytes)
-                             : (uint64_t)(scratch + (size_t)(-s - 1) * blob_bytes);
-            }
-            uptr[ui] = a;
+            uptr[ui] = addr;
         }
         if (is_cold) cold[ci] = e;
         for (int c = 0; c < nchunks; ++c) hist[(size_t)c * stride + e] += off;
@@ -154,16 +118,17 @@ hipError_t launch_group(const GroupArgs &a, char *ws, const WsLayout &L, hipStre
     int32_t *hist = reinterpret_cast<int32_t *>(ws + L.hist);
     int32_t *rank = reinterpret_cast<int32_t *>(ws + L.rank);
     if (L.nchunks > 0) {
-        hipLaunchKernelGGL(group_hist, dim3(L.nchunks), dim3(kChunk), 0, st, a.ids, P, a.E, hist, rank);
+        MOE_LAUNCH("group_hist", group_hist, dim3(L.nchunks), dim3(kChunk), 0, st, a.ids, P, a.E, hist, rank);
     }
-    hipLaunchKernelGGL(group_scan, dim3(1), dim3(1024), 0, st, L.nchunks, a.E, a.slot, a.n_hot, a.n_cold,
+    MOE_LAUNCH("group_scan", group_scan, dim3(1), dim3(1024), 0, st, L.nchunks, a.E, a.slot, a.n_hot, a.n_cold,
                        a.hot_base, a.scratch, a.blob_bytes, hist,
                        reinterpret_cast<int32_t *>(ws + L.counts), reinterpret_cast<int32_t *>(ws + L.nuniq),
                        reinterpret_cast<int32_t *>(ws + L.uniq), reinterpret_cast<int32_t *>(ws + L.ucnt),
                        reinterpret_cast<int32_t *>(ws + L.uoff), reinterpret_cast<uint64_t *>(ws + L.uptr),
-                       reinterpret_cast<int32_t *>(ws + L.cold), reinterpret_cast<int32_t *>(ws + L.status));
+                       reinterpret_cast<int32_t *>(ws + L.cold), reinterpret_cast<int32_t *>(ws + L.status),
+                       reinterpret_cast<int32_t *>(ws + L.sync));
     if (L.nchunks > 0) {
-        hipLaunchKernelGGL(group_place, dim3(L.nchunks), dim3(kChunk), 0, st, a.ids, P, a.E, hist, rank,
+        MOE_LAUNCH("group_place", group_place, dim3(L.nchunks), dim3(kChunk), 0, st, a.ids, P, a.E, hist, rank,
                            reinterpret_cast<int32_t *>(ws + L.plist));
     }
     return hipGetLastError();
@@ -184,7 +149,7 @@ __global__ __launch_bounds__(1024) void pick_set_out(const int32_t *__restrict__
 
 hipError_t launch_pick_set_out(const char *ws, const WsLayout &L, int E, int32_t *counts_out,
                                int32_t *cold_out, hipStream_t st) {
-    hipLaunchKernelGGL(pick_set_out, dim3(1), dim3(1024), 0, st,
+    MOE_LAUNCH("pick_set_out", pick_set_out, dim3(1), dim3(1024), 0, st,
                        reinterpret_cast<const int32_t *>(ws + L.counts),
                        reinterpret_cast<const int32_t *>(ws + L.nuniq),
                        reinterpret_cast<const int32_t *>(ws + L.cold), E, counts_out, cold_out);

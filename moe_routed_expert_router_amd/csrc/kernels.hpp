@@ -1,9 +1,26 @@
 // Internal launchers of the HIP path (one translation unit per kernel family).
 #pragma once
 
+#include <hip/hip_ext.h>
+
 #include "common.hpp"
 
 namespace moe {
+
+// Per-kernel timing (profile.hip).  When enabled, prof_events() hands out a
+// start/stop event pair that the launch itself records (hipExtLaunchKernel
+// stamps them from the dispatch), so the elapsed time is the kernel's own
+// execution time; otherwise it returns false and the launch is plain.
+bool prof_events(const char *name, hipEvent_t *start, hipEvent_t *stop);
+
+#define MOE_LAUNCH(name, kernel, grid, block, shmem, st, ...)                                       \
+    do {                                                                                            \
+        hipEvent_t _moe_e0 = nullptr, _moe_e1 = nullptr;                                            \
+        if (::moe::prof_events((name), &_moe_e0, &_moe_e1))                                         \
+            hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, _moe_e0, _moe_e1, 0, __VA_ARGS__); \
+        else                                                                                        \
+            hipLaunchKernelGGL(kernel, grid, block, shmem, st, __VA_ARGS__);                        \
+    } while (0)
 
 // Router logits z[T][E] = x Wr^T + bias (fp32 accumulation).
 hipError_t launch_route_logits(const uint16_t *x, const float *wr, const float *bias,
@@ -25,6 +42,11 @@ struct GroupArgs {
 };
 hipError_t launch_group(const GroupArgs &a, char *ws, const WsLayout &L, hipStream_t st);
 
+// Decode path (T*k <= 1024): top-k of every token and the whole pick set in
+// one single-block launch.
+hipError_t launch_select_group_small(const float *z, int T, int k, int renorm, int32_t *ids, float *w,
+                                     const GroupArgs &a, char *ws, const WsLayout &L, hipStream_t st);
+
 // Copies counts [E] and the picked-cold list [E+1] out of a grouped workspace.
 hipError_t launch_pick_set_out(const char *ws, const WsLayout &L, int E,
                                int32_t *counts_out, int32_t *cold_out, hipStream_t st);
@@ -44,5 +66,12 @@ struct FfnArgs {
     void *out;
 };
 hipError_t launch_ffn(const FfnArgs &a, char *ws, const WsLayout &L, hipStream_t st);
+
+// True when launch_ffn uses the block kernels (decode sizes), whose combine is
+// fused into the down projection.
+bool ffn_block_path(int T, int H, int I);
+
+// Largest T routed by the single-block select-and-group kernel.
+constexpr int kSmallRouteTokens = 32;
 
 }  // namespace moe

@@ -50,7 +50,8 @@ class Layer:
     """One layer of a workload, resident as the workload says."""
 
     def __init__(self, wl: gen.Workload, layer: int = 0, T: int | None = None, scratch=None,
-                 all_hot: bool = False, cal: dict | None = None, coherent: bool = False):
+                 all_hot: bool = False, cal: dict | None = None, coherent: bool = False,
+                 hot: list | None = None):
         self.wl, self.layer = wl, layer
         H, I, E, k = wl.hidden, wl.inter, wl.n_experts, wl.top_k
         self.H, self.I, self.E, self.k = H, I, E, k
@@ -64,7 +65,9 @@ class Layer:
         if wl.zipf:
             cal = cal or gen.load_calibration()
             self.bias_np = gen.zipf_prior(seed, layer, E, cal["alpha"])
-        if wl.n_hot is None or all_hot:
+        if hot is not None:
+            hot = list(hot)
+        elif wl.n_hot is None or all_hot:
             hot = list(range(E))
         else:
             hot = gen.hot_set(seed, layer, cal)

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe.h")
 
 moe = pytest.importorskip("moe_routed_expert_router_amd",
-                          reason="libmoe.so not built (python -m moe_routed_expert_router_amd.build)")
+                          reason="libmoe.so not built (python moe_routed_expert_router_amd/build.py)")
 
 
 def _declared():

@@ -286,3 +286,32 @@ def test_gpu_error_paths():
     st = lib.moe_route(ctypes.byref(L.shape), 4, L.x.data_ptr() + 2, L.wr.data_ptr(), None, 1,
                        L.ids.data_ptr(), L.w.data_ptr(), None, L.ws.data_ptr(), 16, None)
     assert st == moe.MOE_ERR_MISALIGNED
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 8), ("hotcold8", 8)])
+def test_graph_replay_matches_eager(name, T):
+    """The layer captured in a HIP graph gives the eager result on every
+    replay, with eager work and synchronisations between replays."""
+    L = Layer(gen.workload(name), T=T)
+    try:
+        eager = L.forward().clone()
+        eager_ids = L.ids.clone()
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s, capture_error_mode="relaxed"):
+            moe.moe_layer_forward(L.shape, L.x, L.wr, L.bias, True, L.residency, L.ids, L.w, L.out, L.ws, s)
+        torch.cuda.synchronize()
+        for i in range(4):
+            L.out.fill_(float(i))
+            L.ids.fill_(-7)
+            if L.scratch is not None:
+                L.scratch.fill_(0x33)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(L.ids, eager_ids), i
+            assert torch.equal(L.out, eager), i
+    finally:
+        L.close()
