@@ -265,6 +265,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batch8", action="store_true", help="skip the batch-8 hot/cold secondary figures")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="first run one plain float64 copy of this many MiB (a known-size kernel for "
+                         "scaling hardware byte counters)")
     a = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -279,6 +282,15 @@ def main():
         sys.exit(2)
     import moe_routed_expert_router_amd as moe  # noqa: F401  (fails loudly if libmoe.so is missing)
 
+    if a.copy_probe_mb:
+        n = a.copy_probe_mb * (1 << 20) // 8
+        src = torch.ones(n, dtype=torch.float64, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: {a.copy_probe_mb} MiB read + {a.copy_probe_mb} MiB written")
+        del src, dst
     log(f"[bench] workload {a.workload}: setup")
     w, secs, steps, graphed, prof, by = measure(a.workload, a.steps, a.warmup, a.reps, not a.no_graph,
                                                 min(a.steps, 256))
