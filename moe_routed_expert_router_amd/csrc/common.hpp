@@ -42,7 +42,7 @@ struct WsLayout {
     size_t sync;       // int32 [kSyncWords]: FFN completion counters (zeroed by the grouping)
     size_t logits;     // float [T][E]
     size_t status;     // int32 [16]: [0] invalid-pair count, [1] bad-residency count
-    size_t nuniq;      // int32 [4]: [0] distinct experts U, [1] picked-cold count
+    size_t nuniq;      // int32 [4]: [0] distinct experts U, [1] picked-cold count, [2] token tiles
     size_t uniq;       // int32 [E]: distinct picked experts, increasing
     size_t ucnt;       // int32 [E]: pairs per distinct expert
     size_t uoff;       // int32 [E+1]: start of each expert's run in plist
@@ -52,6 +52,7 @@ struct WsLayout {
     size_t hist;       // int32 [nchunks][E+1]: per-chunk counts (+ bad ids), then chunk bases
     size_t rank;       // int32 [P]: rank of a pair among its chunk's pairs of that expert
     size_t plist;      // int32 [P]: pair ids t*k+j grouped by expert, increasing inside
+    size_t tlist;      // int32 [max_tiles]: token tiles, distinct-expert index | part << 10
     size_t hbuf;       // uint16 [2][P][I]: SwiGLU output split as bf16 hi and lo parts
     size_t ybuf;       // float [P][H]: per-pair expert outputs
     size_t total;
@@ -59,6 +60,13 @@ struct WsLayout {
 
     static constexpr int kChunk = 256;      // pairs per grouping chunk
     static constexpr int kSyncWords = 4096;  // >= H/32 for H <= 65536 (+ spare)
+    static constexpr int kPrefillTokens = 160;  // tokens per tile of the grouped GEMM
+
+    // Upper bound on the token tiles of P pairs over E experts.
+    static int max_tiles(int E, size_t P) {
+        const size_t u = (size_t)E < P ? (size_t)E : P;
+        return (int)(u + (P + kPrefillTokens - 1) / kPrefillTokens);
+    }
 
     static size_t up(size_t v) { return (v + 255) & ~(size_t)255; }
     static WsLayout make(int H, int I, int E, int k, int T) {
@@ -80,6 +88,7 @@ struct WsLayout {
         w.hist = take((size_t)w.nchunks * (E + 1) * 4);
         w.rank = take(P * 4);
         w.plist = take(P * 4);
+        w.tlist = take((size_t)max_tiles(E, P) * 4);
         w.hbuf = take(2 * P * (size_t)I * 2);
         w.ybuf = take(P * (size_t)H * 4);
         w.total = o;
@@ -97,11 +106,12 @@ struct GroupView {
     const uint64_t *uptr;
     const int32_t *plist;
     const int32_t *cold;
+    const int32_t *tlist;
 };
 
 // Mutable view of the grouping outputs, for the kernels that write them.
 struct GroupOut {
-    int32_t *sync, *status, *counts, *nuniq, *uniq, *ucnt, *uoff, *cold, *plist;
+    int32_t *sync, *status, *counts, *nuniq, *uniq, *ucnt, *uoff, *cold, *plist, *tlist;
     uint64_t *uptr;
     static GroupOut at(char *ws, const WsLayout &L) {
         GroupOut o;
@@ -114,6 +124,7 @@ struct GroupOut {
         o.uoff = reinterpret_cast<int32_t *>(ws + L.uoff);
         o.cold = reinterpret_cast<int32_t *>(ws + L.cold);
         o.plist = reinterpret_cast<int32_t *>(ws + L.plist);
+        o.tlist = reinterpret_cast<int32_t *>(ws + L.tlist);
         o.uptr = reinterpret_cast<uint64_t *>(ws + L.uptr);
         return o;
     }
@@ -129,6 +140,7 @@ inline GroupView group_view(char *ws, const WsLayout &L) {
     v.uptr = reinterpret_cast<const uint64_t *>(ws + L.uptr);
     v.plist = reinterpret_cast<const int32_t *>(ws + L.plist);
     v.cold = reinterpret_cast<const int32_t *>(ws + L.cold);
+    v.tlist = reinterpret_cast<const int32_t *>(ws + L.tlist);
     return v;
 }
 

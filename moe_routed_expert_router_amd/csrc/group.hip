@@ -51,7 +51,8 @@ __global__ __launch_bounds__(1024) void group_scan(int nchunks, int E, const int
                                                    int32_t *__restrict__ nuniq, int32_t *__restrict__ uniq,
                                                    int32_t *__restrict__ ucnt, int32_t *__restrict__ uoff,
                                                    uint64_t *__restrict__ uptr, int32_t *__restrict__ cold,
-                                                   int32_t *__restrict__ status, int32_t *__restrict__ sync) {
+                                                   int32_t *__restrict__ status, int32_t *__restrict__ sync,
+                                                   int32_t *__restrict__ tlist) {
     __shared__ int lds[40];
     const int e = threadIdx.x;
     for (int i = e; i < WsLayout::kSyncWords; i += 1024) sync[i] = 0;
@@ -80,6 +81,11 @@ __global__ __launch_bounds__(1024) void group_scan(int nchunks, int E, const int
     const int ci = block_exscan1024(is_cold ? 1 : 0, lds, &nc);
     int nbad;
     block_exscan1024((picked && !ok) ? 1 : 0, lds, &nbad);
+    // token tiles of the grouped GEMM: expert order, kPrefillTokens pairs each
+    const int ntile = (cnt + WsLayout::kPrefillTokens - 1) / WsLayout::kPrefillTokens;
+    int ntiles;
+    const int toff = block_exscan1024(ntile, lds, &ntiles);
+    for (int part = 0; part < ntile; ++part) tlist[toff + part] = ui | (part << 10);
     if (is_exp) {
         counts[e] = cnt;
         if (picked) {
@@ -97,6 +103,7 @@ __global__ __launch_bounds__(1024) void group_scan(int nchunks, int E, const int
         status[0] = bad;
         nuniq[0] = nu;
         nuniq[1] = nc;
+        nuniq[2] = ntiles;
         status[1] = nbad;
         uoff[nu] = ntot;
     }
@@ -126,7 +133,7 @@ hipError_t launch_group(const GroupArgs &a, char *ws, const WsLayout &L, hipStre
                        reinterpret_cast<int32_t *>(ws + L.uniq), reinterpret_cast<int32_t *>(ws + L.ucnt),
                        reinterpret_cast<int32_t *>(ws + L.uoff), reinterpret_cast<uint64_t *>(ws + L.uptr),
                        reinterpret_cast<int32_t *>(ws + L.cold), reinterpret_cast<int32_t *>(ws + L.status),
-                       reinterpret_cast<int32_t *>(ws + L.sync));
+                       reinterpret_cast<int32_t *>(ws + L.sync), reinterpret_cast<int32_t *>(ws + L.tlist));
     if (L.nchunks > 0) {
         MOE_LAUNCH("group_place", group_place, dim3(L.nchunks), dim3(kChunk), 0, st, a.ids, P, a.E, hist, rank,
                            reinterpret_cast<int32_t *>(ws + L.plist));

@@ -67,9 +67,16 @@ struct FfnArgs {
 };
 hipError_t launch_ffn(const FfnArgs &a, char *ws, const WsLayout &L, hipStream_t st);
 
-// True when launch_ffn uses the block kernels (decode sizes), whose combine is
-// fused into the down projection.
+// True when launch_ffn uses the block kernels (decode sizes).
 bool ffn_block_path(int T, int H, int I);
+
+// True when launch_ffn uses the grouped-GEMM kernels (prefill sizes).
+bool ffn_gemm_path(int T, int H, int I);
+
+// Grouped-GEMM gate/up + SwiGLU and down over the token tiles of the grouping
+// (h as bf16 hi/lo planes indexed by grouped position, y by pair id).
+hipError_t launch_ffn_gemm(const FfnArgs &a, const GroupView &gv, int max_tiles, uint16_t *hhi, uint16_t *hlo,
+                           float *y, hipStream_t st);
 
 // Largest T routed by the single-block select-and-group kernel.
 constexpr int kSmallRouteTokens = 32;
