@@ -12,6 +12,7 @@ namespace moe {
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
@@ -201,6 +202,12 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
 
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 32x32x16 bf16 MFMA.  A lane l: A[l % 32][8 (l / 32) + i]; B lane l:
+// B[8 (l / 32) + i][l % 32]; D lane l, element i: D[8 (i / 4) + 4 (l / 32) + i % 4][l % 32].
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ float silu(float g) {

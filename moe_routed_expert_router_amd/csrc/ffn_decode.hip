@@ -484,7 +484,7 @@ hipError_t launch_ffn(const FfnArgs &a, char *ws, const WsLayout &L, hipStream_t
     uint16_t *hlo = hhi + P * (size_t)a.I;
     float *y = reinterpret_cast<float *>(ws + L.ybuf);
 
-    if (ffn_gemm_path(a.T, a.H, a.I)) {
+    if (ffn_gemm_path(a.T, a.H, a.I, a.k)) {
         const hipError_t e = launch_ffn_gemm(a, gv, WsLayout::max_tiles(a.E, P), hhi, hlo, y, st);
         if (e != hipSuccess) return e;
     } else if (ffn_block_path(a.T, a.H, a.I)) {

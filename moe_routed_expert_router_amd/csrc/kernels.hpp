@@ -71,7 +71,7 @@ hipError_t launch_ffn(const FfnArgs &a, char *ws, const WsLayout &L, hipStream_t
 bool ffn_block_path(int T, int H, int I);
 
 // True when launch_ffn uses the grouped-GEMM kernels (prefill sizes).
-bool ffn_gemm_path(int T, int H, int I);
+bool ffn_gemm_path(int T, int H, int I, int k);
 
 // Grouped-GEMM gate/up + SwiGLU and down over the token tiles of the grouping
 // (h as bf16 hi/lo planes indexed by grouped position, y by pair id).

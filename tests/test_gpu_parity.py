@@ -93,8 +93,7 @@ def test_device_generator_matches_cpu():
 
 @pytest.mark.parametrize("T", [4, 1, 3, 17, 37, 300, 1000])
 def test_tiny_layer(T):
-    """T <= 32: decode kernels; T > 32: grouped GEMM (T=1000 gives each of the
-    8 experts ~250 pairs, so two token tiles, the second one ragged)."""
+    """T <= 32: decode kernels; T > 32 at this shape (H=256): one-wave kernels."""
     L = Layer(gen.workload("tiny"), T=T)
     ids_g, w_g, z_g = route_on_gpu(L)
     check_route(L, ids_g, w_g, z_g)
@@ -236,6 +235,23 @@ def test_gemm_hot_cold_equals_all_hot_and_oracle():
         check_out(a.cpu().numpy(), ref["out"])
     finally:
         mixed.close()
+
+
+@pytest.mark.parametrize("E,k,T", [(64, 2, 2000), (64, 2, 3000), (32, 4, 1100), (16, 3, 700)])
+def test_gemm_tile_shapes(E, k, T):
+    """Grouped-GEMM path (H=512, I=256) at token counts per expert that give
+    every number of 32-token column tiles (1..5) and ragged last tiles."""
+    wl = gen.Workload("gemm_shapes", 512, 256, E, k, T, seed=E + k)
+    L = Layer(wl)
+    out = L.forward()
+    torch.cuda.synchronize()
+    ids = L.ids.cpu().numpy()
+    counts = np.bincount(ids.reshape(-1), minlength=E)
+    tiles = np.concatenate([[min(160, c - p) for p in range(0, c, 160)] for c in counts if c > 0])
+    print(f"E={E} k={k} T={T}: column tiles per token tile {sorted(set(((tiles + 31) // 32).tolist()))}")
+    ref = oracle_out(L)
+    assert np.array_equal(ids, ref["ids"])
+    check_out(out.cpu().numpy(), ref["out"])
 
 
 def test_wave_path_for_unaligned_hidden():
