@@ -119,49 +119,77 @@ __device__ __forceinline__ int block_exscan1024(int v, int *lds, int *tot) {
 
 constexpr int kPerLane = kMaxExperts / kWave;
 
-// Top-k of one token's E logits by one wave: k rounds of a wave arg-max whose
-// order is (larger value, then lower index), so the picks are the k largest
-// logits with ties to the lower expert index, in decreasing order; NaN orders
-// as -inf.  Pick j ends in lane j (k <= 32), which returns its expert and
-// softmax weight (renormalised over the k picks, or over all E).
-__device__ __forceinline__ void topk_wave(const float *__restrict__ zr, int E, int k, int renorm,
-                                          int *pick_e, float *pick_w) {
+// Order-preserving map of a float to uint32 (larger float -> larger key); NaN
+// maps like -inf.  key_to_float inverts it.
+__device__ __forceinline__ uint32_t float_key(float v) {
+    const uint32_t u = (v == v) ? __float_as_uint(v) : 0xff800000u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// One step of the wave-wide maximum of 64-bit keys: lanes the DPP control
+// (with row mask RM) does not write keep their own key.
+template <int CTRL, int RM>
+__device__ __forceinline__ uint64_t kmax_step(uint64_t key) {
+    const uint32_t hi = (uint32_t)(key >> 32), lo = (uint32_t)key;
+    const uint32_t oh = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, RM, 0xf, false);
+    const uint32_t ol = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, RM, 0xf, false);
+    const uint64_t o = ((uint64_t)oh << 32) | ol;
+    return o > key ? o : key;
+}
+
+// Maximum key over the wave, in every lane: butterflies inside each row of
+// 16 lanes, then row 0 -> 1 and 2 -> 3 (row_bcast:15), then rows 0..1 -> 3
+// (row_bcast:31); lane 63 ends with the maximum and is read back uniformly.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t key) {
+    key = kmax_step<kDppXor1, 0xf>(key);
+    key = kmax_step<kDppXor2, 0xf>(key);
+    key = kmax_step<kDppHalfMirror, 0xf>(key);
+    key = kmax_step<kDppMirror, 0xf>(key);
+    key = kmax_step<0x142, 0xa>(key);
+    key = kmax_step<0x143, 0xc>(key);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(key >> 32), 63);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)key, 63);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Top-k of one token's E logits by one wave (NPL >= E / 64 values per lane).
+// Each logit becomes the 64-bit key (float_key(z), E - 1 - e), so the key
+// order is: larger logit first, equal logits by lower expert index; NaN
+// orders as -inf.  k rounds take the wave maximum and clear it (key 0 is
+// below every real key).  Pick j (k <= 32) ends in lane j, which returns its
+// expert and softmax weight (renormalised over the k picks, or over all E).
+template <int NPL>
+__device__ __forceinline__ void topk_wave(const float *__restrict__ zr, int E, int k, int renorm, int *pick_e,
+                                          float *pick_w) {
     const int lane = threadIdx.x & 63;
-    float v[kPerLane];
-    uint32_t taken = 0;
-    // issue every load before looking at any value (the guard is wave-uniform)
+    float v[NPL];
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i) {
+    for (int i = 0; i < NPL; ++i) {   // every load before any use (the guard is wave-uniform)
         const int e = lane + 64 * i;
         v[i] = (64 * i < E) ? zr[e < E ? e : 0] : -INFINITY;
     }
+    uint64_t key[NPL];
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i) {
+    for (int i = 0; i < NPL; ++i) {
         const int e = lane + 64 * i;
-        const float a = v[i];
-        v[i] = (e < E && a == a) ? a : -INFINITY;
-        taken |= (e < E ? 0u : 1u) << i;
+        v[i] = (e < E && v[i] == v[i]) ? v[i] : -INFINITY;
+        key[i] = e < E ? (((uint64_t)float_key(v[i]) << 32) | (uint32_t)(E - 1 - e)) : 0;
     }
-    float my_v = -INFINITY;
-    int my_e = 0;
+    uint64_t mine = 0;
     for (int j = 0; j < k; ++j) {
-        float bv = -INFINITY;
-        int be = 0x7fffffff;
+        uint64_t best = key[0];
 #pragma unroll
-        for (int i = 0; i < kPerLane; ++i) {   // branch-free local arg-max
-            const int e = lane + 64 * i;
-            const bool free_ = ((taken >> i) & 1u) == 0u;
-            const bool win = free_ & ((v[i] > bv) | ((v[i] == bv) & (e < be)));
-            bv = win ? v[i] : bv;
-            be = win ? e : be;
-        }
-        wave_argmax(bv, be);
-        if ((be & 63) == lane) taken |= 1u << (be >> 6);
-        if (lane == j) {
-            my_v = bv;
-            my_e = be;
-        }
+        for (int i = 1; i < NPL; ++i) best = key[i] > best ? key[i] : best;
+        const uint64_t win = wave_max_key(best);
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) key[i] = key[i] == win ? 0 : key[i];
+        mine = lane == j ? win : mine;
     }
+    const float my_v = key_to_float((uint32_t)(mine >> 32));
+    const int my_e = E - 1 - (int)(uint32_t)mine;
     const float m = readlanef(my_v, 0);
     const float p = (lane < k) ? expf(my_v - m) : 0.0f;
     float s;
@@ -170,12 +198,18 @@ __device__ __forceinline__ void topk_wave(const float *__restrict__ zr, int E, i
     } else {
         float a = 0.0f;
 #pragma unroll
-        for (int i = 0; i < kPerLane; ++i)
+        for (int i = 0; i < NPL; ++i)
             if (lane + 64 * i < E) a += expf(v[i] - m);
         s = wave_sum(a);
     }
-    *pick_e = my_e;
+    *pick_e = lane < k ? my_e : 0;
     *pick_w = p / s;
+}
+
+// Values per lane for E experts: ceil(E / 64) rounded up to 1, 2, 4, 8 or 16.
+inline int topk_npl(int E) {
+    const int n = (E + 63) / 64;
+    return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : n <= 8 ? 8 : 16;
 }
 
 // Blob address of expert e per the residency table, or 0 when its entry does

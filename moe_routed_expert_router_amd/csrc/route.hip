@@ -11,71 +11,63 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Decode-size logits (T <= 32): a block of 4 waves owns 4 expert rows; tokens
-// are staged in LDS 8 at a time and each wave issues its whole row (up to
-// 4096 columns, 16 x 128-bit loads per lane) before the first FMA, so the
-// router matrix (E*H*4 bytes, the only HBM traffic) streams with every load
-// in flight at once.
-// ---------------------------------------------------------------------------
-constexpr int kGemvTok = 8;
-constexpr int kGemvCols = 4096;   // columns per register pass
+// Router logits for few tokens (T <= 32).  One block per expert row; its
+// four waves take a quarter of the row each (lane l: the float4 chunks
+// l + 64 i of its quarter), issue every weight and token load before using
+// any, and accumulate fp32 products per token.  Per token, a wave sum and
+// then the four wave partials added in wave order give the logit, so the
+// result is reproducible.  Tokens go in passes of kRtTok.  NC >= H / 1024
+// chunks per lane.
+constexpr int kRtTok = 8;
 
-__global__ __launch_bounds__(256) void route_logits_gemv(
-    const uint16_t *__restrict__ x, const float *__restrict__ wr, const float *__restrict__ bias,
-    int T, int H, int E, float *__restrict__ z) {
-    extern __shared__ __align__(16) uint16_t xs[];   // [kGemvTok][min(H, kGemvCols)]
-    const int lane = threadIdx.x & 63;
-    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const bool ve = e < E;
-    const float4 *wrow = reinterpret_cast<const float4 *>(wr + (size_t)(ve ? e : 0) * H);
-    const float b = (ve && bias) ? bias[e] : 0.0f;
-    const int W = H < kGemvCols ? H : kGemvCols;   // staged columns per pass
-    for (int t0 = 0; t0 < T; t0 += kGemvTok) {
-        const int nt = (T - t0) < kGemvTok ? (T - t0) : kGemvTok;
-        float acc[kGemvTok];
+template <int NC>
+__global__ __launch_bounds__(256) void route_logits_small(const uint16_t *__restrict__ x, const float *__restrict__ wr,
+                                                          const float *__restrict__ bias, int T, int H, int E,
+                                                          float *__restrict__ z) {
+    __shared__ float part[4][kRtTok];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int e = blockIdx.x;
+    const int nch = H / 4;   // float4 chunks of the row
+    const float4 *wrow = reinterpret_cast<const float4 *>(wr + (size_t)e * H);
+    float4 w4[NC];
 #pragma unroll
-        for (int i = 0; i < kGemvTok; ++i) acc[i] = 0.0f;
-        for (int h0 = 0; h0 < H; h0 += W) {
-            __syncthreads();
-            const int n16 = nt * (W / 8);   // 16-byte chunks of the token tile
-            for (int i = threadIdx.x; i < n16; i += 256) {
-                const int tt = i / (W / 8), c = i - tt * (W / 8);
-                reinterpret_cast<uint4 *>(xs)[i] =
-                    *reinterpret_cast<const uint4 *>(x + (size_t)(t0 + tt) * H + h0 + 8 * c);
+    for (int i = 0; i < NC; ++i) {
+        const int c = wave * 64 + lane + 256 * i;
+        w4[i] = c < nch ? wrow[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    const float b = bias ? bias[e] : 0.0f;
+    for (int t0 = 0; t0 < T; t0 += kRtTok) {
+        const int nt = (T - t0) < kRtTok ? (T - t0) : kRtTok;
+        uint2 xv[kRtTok][NC];
+#pragma unroll
+        for (int tt = 0; tt < kRtTok; ++tt)
+#pragma unroll
+            for (int i = 0; i < NC; ++i) {
+                const int c = wave * 64 + lane + 256 * i;
+                xv[tt][i] = (tt < nt && c < nch)
+                                ? *reinterpret_cast<const uint2 *>(x + (size_t)(t0 + tt) * H + 4 * c)
+                                : make_uint2(0u, 0u);
             }
-            __syncthreads();
-            if (ve) {
-                float4 w4[kGemvCols / 256];
 #pragma unroll
-                for (int i = 0; i < kGemvCols / 256; ++i) {
-                    const int c = lane + 64 * i;
-                    w4[i] = (4 * c < W) ? wrow[h0 / 4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
-                }
+        for (int tt = 0; tt < kRtTok; ++tt) {
+            float a = 0.0f;
 #pragma unroll
-                for (int tt = 0; tt < kGemvTok; ++tt) {
-                    if (tt < nt) {
-                        float a = acc[tt];
-#pragma unroll
-                        for (int i = 0; i < kGemvCols / 256; ++i) {
-                            const int c = lane + 64 * i;
-                            if (4 * c < W) {
-                                const uint2 xv = reinterpret_cast<const uint2 *>(xs + tt * W)[c];
-                                a = fmaf(w4[i].x, bf16_bits_to_f32(xv.x & 0xffffu), a);
-                                a = fmaf(w4[i].y, bf16_bits_to_f32(xv.x >> 16), a);
-                                a = fmaf(w4[i].z, bf16_bits_to_f32(xv.y & 0xffffu), a);
-                                a = fmaf(w4[i].w, bf16_bits_to_f32(xv.y >> 16), a);
-                            }
-                        }
-                        acc[tt] = a;
-                    }
-                }
+            for (int i = 0; i < NC; ++i) {
+                a = fmaf(w4[i].x, bf16_bits_to_f32(xv[tt][i].x & 0xffffu), a);
+                a = fmaf(w4[i].y, bf16_bits_to_f32(xv[tt][i].x >> 16), a);
+                a = fmaf(w4[i].z, bf16_bits_to_f32(xv[tt][i].y & 0xffffu), a);
+                a = fmaf(w4[i].w, bf16_bits_to_f32(xv[tt][i].y >> 16), a);
+            }
+            if (tt < nt) {
+                const float v = wave_sum(a);
+                if (lane == 0) part[wave][tt] = v;
             }
         }
-#pragma unroll
-        for (int tt = 0; tt < kGemvTok; ++tt) {
-            const float v = wave_sum(acc[tt]);
-            if (ve && lane == 0 && tt < nt) z[(size_t)(t0 + tt) * E + e] = v + b;
-        }
+        __syncthreads();
+        if (threadIdx.x < nt)
+            z[(size_t)(t0 + threadIdx.x) * E + e] =
+                ((part[0][threadIdx.x] + part[1][threadIdx.x]) + (part[2][threadIdx.x] + part[3][threadIdx.x])) + b;
+        __syncthreads();
     }
 }
 
@@ -168,10 +160,21 @@ __global__ __launch_bounds__(256) void route_logits_mfma(
 hipError_t launch_route_logits(const uint16_t *x, const float *wr, const float *bias,
                                int T, int H, int E, float *z, hipStream_t st) {
     if (T <= 32) {
-        const int W = H < kGemvCols ? H : kGemvCols;
-        const size_t lds = (size_t)kGemvTok * W * 2;
-        MOE_LAUNCH("route_logits_gemv", route_logits_gemv, dim3((E + 3) / 4), dim3(256), lds, st,
-                   x, wr, bias, T, H, E, z);
+        const int nc = (H + 1023) / 1024;   // float4 chunks per lane
+        const dim3 g(E), b(256);
+        if (nc <= 1)
+            MOE_LAUNCH("route_logits_small", route_logits_small<1>, g, b, 0, st, x, wr, bias, T, H, E, z);
+        else if (nc <= 2)
+            MOE_LAUNCH("route_logits_small", route_logits_small<2>, g, b, 0, st, x, wr, bias, T, H, E, z);
+        else if (nc <= 4)
+            MOE_LAUNCH("route_logits_small", route_logits_small<4>, g, b, 0, st, x, wr, bias, T, H, E, z);
+        else if (nc <= 8)
+            MOE_LAUNCH("route_logits_small", route_logits_small<8>, g, b, 0, st, x, wr, bias, T, H, E, z);
+        else if (nc <= 16)
+            MOE_LAUNCH("route_logits_small", route_logits_small<16>, g, b, 0, st, x, wr, bias, T, H, E, z);
+        else
+            MOE_LAUNCH("route_logits_mfma", route_logits_mfma, dim3((E + 63) / 64, (T + 63) / 64), dim3(256), 0,
+                       st, x, wr, bias, T, H, E, z);
     } else {
         MOE_LAUNCH("route_logits_mfma", route_logits_mfma, dim3((E + 63) / 64, (T + 63) / 64), dim3(256), 0, st,
                    x, wr, bias, T, H, E, z);
@@ -182,6 +185,7 @@ hipError_t launch_route_logits(const uint16_t *x, const float *wr, const float *
 // ---------------------------------------------------------------------------
 // Top-k for any T: one wave per token.
 // ---------------------------------------------------------------------------
+template <int NPL>
 __global__ __launch_bounds__(256) void route_topk(const float *__restrict__ z, int T, int E, int k,
                                                   int renorm, int32_t *__restrict__ ids,
                                                   float *__restrict__ w) {
@@ -190,7 +194,7 @@ __global__ __launch_bounds__(256) void route_topk(const float *__restrict__ z, i
     if (t >= T) return;
     int pe;
     float pw;
-    topk_wave(z + (size_t)t * E, E, k, renorm, &pe, &pw);
+    topk_wave<NPL>(z + (size_t)t * E, E, k, renorm, &pe, &pw);
     if (lane < k) {
         ids[(size_t)t * k + lane] = pe;
         w[(size_t)t * k + lane] = pw;
@@ -199,113 +203,100 @@ __global__ __launch_bounds__(256) void route_topk(const float *__restrict__ z, i
 
 hipError_t launch_topk(const float *z, int T, int E, int k, int renorm, int32_t *ids, float *w,
                        hipStream_t st) {
-    MOE_LAUNCH("route_topk", route_topk, dim3((T + 3) / 4), dim3(256), 0, st, z, T, E, k, renorm, ids, w);
+    const dim3 g((T + 3) / 4), b(256);
+    switch (topk_npl(E)) {
+        case 1: MOE_LAUNCH("route_topk", route_topk<1>, g, b, 0, st, z, T, E, k, renorm, ids, w); break;
+        case 2: MOE_LAUNCH("route_topk", route_topk<2>, g, b, 0, st, z, T, E, k, renorm, ids, w); break;
+        case 4: MOE_LAUNCH("route_topk", route_topk<4>, g, b, 0, st, z, T, E, k, renorm, ids, w); break;
+        case 8: MOE_LAUNCH("route_topk", route_topk<8>, g, b, 0, st, z, T, E, k, renorm, ids, w); break;
+        default: MOE_LAUNCH("route_topk", route_topk<16>, g, b, 0, st, z, T, E, k, renorm, ids, w); break;
+    }
     return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// Decode path: top-k of every token and the whole pick set in ONE block, so
-// routing and grouping cost one launch.  16 waves take the tokens and count
-// each pick into its expert (LDS integer atomics: only the counts are used).
-// Wave 0 then walks the experts in increasing order — lane l owns a
-// contiguous run of E/64 experts — and with three wave scans turns the counts
-// into each expert's pair run, the distinct-expert list with blob addresses,
-// and the picked-cold list.  Finally one thread per pair ranks it among the
-// earlier pairs of its expert, so every run lists pairs in increasing order.
-// It also zeroes the FFN's completion counters.  Needs T*k <= 1024.
-// ---------------------------------------------------------------------------
+// Decode path (T * k <= 1024 pairs): top-k of every token (one wave per
+// token) and the whole pick set in one single-block launch.  The grouping is
+// computed from the pair side: pair p of expert e goes to position
+// #{pairs of smaller experts} + #{earlier pairs of e} of the pair list; the
+// first pair of each expert writes its distinct-expert entry (index = number
+// of distinct smaller experts) and, if it is cold, its cold-list entry.
+template <int NPL>
 __global__ __launch_bounds__(1024) void select_group_small(
     const float *__restrict__ z, int T, int E, int k, int renorm, int32_t *__restrict__ ids,
     float *__restrict__ w, const int32_t *__restrict__ slot, int n_hot, int n_cold, const uint8_t *hot_base,
     const uint8_t *scratch, size_t blob_bytes, GroupOut o) {
     __shared__ int sid[1024];
-    __shared__ int cnt[kMaxExperts];
-    __shared__ int offs[kMaxExperts];
-    __shared__ int sslot[kMaxExperts];
+    __shared__ int sflag[1024];   // per pair: 1 first of its expert, 2 that expert is cold, 4 unusable
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (tid < E) {
-        sslot[tid] = slot[tid];
-        cnt[tid] = 0;
-    }
-    for (int i = tid; i < WsLayout::kSyncWords; i += 1024) o.sync[i] = 0;
-    __syncthreads();
     for (int t = wave; t < T; t += 16) {
         int pe;
         float pw;
-        topk_wave(z + (size_t)t * E, E, k, renorm, &pe, &pw);
+        topk_wave<NPL>(z + (size_t)t * E, E, k, renorm, &pe, &pw);
         if (lane < k) {
             ids[(size_t)t * k + lane] = pe;
             w[(size_t)t * k + lane] = pw;
             sid[t * k + lane] = pe;
-            atomicAdd(&cnt[pe], 1);
         }
     }
     __syncthreads();
     const int P = T * k;
-    if (wave == 0) {
-        const int per = (E + 63) >> 6;   // experts per lane, <= 16
-        const int e0 = lane * per;
-        int c[kPerLane];
-        int tot = 0, npick = 0, ncold = 0, nbad = 0;
-#pragma unroll
-        for (int i = 0; i < kPerLane; ++i) {
-            const int e = e0 + i;
-            c[i] = (i < per && e < E) ? cnt[e] : 0;
-            if (c[i] > 0) {
-                bool ok, cold;
-                (void)expert_address(sslot[e], n_hot, n_cold, hot_base, scratch, blob_bytes, &ok, &cold);
-                npick += 1;
-                ncold += (ok && cold) ? 1 : 0;
-                nbad += ok ? 0 : 1;
-            }
-            tot += c[i];
-        }
-        int ptot, nu, nc;
-        int off = wave_exscan(tot, &ptot);
-        int ui = wave_exscan(npick, &nu);
-        int ci = wave_exscan(ncold, &nc);
-        const int nb = wave_sum_int(nbad);
-#pragma unroll
-        for (int i = 0; i < kPerLane; ++i) {
-            const int e = e0 + i;
-            if (i < per && e < E) {
-                offs[e] = off;
-                o.counts[e] = c[i];
-                if (c[i] > 0) {
-                    bool ok, cold;
-                    const uint64_t addr =
-                        expert_address(sslot[e], n_hot, n_cold, hot_base, scratch, blob_bytes, &ok, &cold);
-                    o.uniq[ui] = e;
-                    o.ucnt[ui] = c[i];
-                    o.uoff[ui] = off;
-                    o.uptr[ui] = addr;
-                    ++ui;
-                    if (ok && cold) o.cold[ci++] = e;
-                }
-                off += c[i];
-            }
-        }
-        if (lane == 0) {
-            o.nuniq[0] = nu;
-            o.nuniq[1] = nc;
-            o.status[0] = 0;
-            o.status[1] = nb;
-            o.uoff[nu] = ptot;
-        }
-    }
-    __syncthreads();
+    int e = 0, lt = 0, eqb = 0, cnt = 0, flag = 0;
+    uint64_t addr = 0;
     if (tid < P) {
-        const int e = sid[tid];
-        int rank = 0;
-        for (int q = 0; q < tid; ++q) rank += (sid[q] == e);
-        o.plist[offs[e] + rank] = tid;
+        e = sid[tid];
+        for (int q = 0; q < P; ++q) {
+            const int eq = sid[q];
+            lt += eq < e;
+            cnt += eq == e;
+            eqb += (eq == e) & (q < tid);
+        }
+        if (eqb == 0) {
+            bool ok, cold;
+            addr = expert_address(slot[e], n_hot, n_cold, hot_base, scratch, blob_bytes, &ok, &cold);
+            flag = 1 | ((ok && cold) ? 2 : 0) | (ok ? 0 : 4);
+        }
+        sflag[tid] = flag;
+        o.plist[lt + eqb] = tid;
+    }
+    const int nu = __syncthreads_count(flag & 1);
+    const int nc = __syncthreads_count(flag & 2);
+    const int nb = __syncthreads_count(flag & 4);
+    if (flag & 1) {
+        int ui = 0, ci = 0;
+        for (int q = 0; q < P; ++q) {
+            const int fq = sflag[q], less = sid[q] < e;
+            ui += (fq & 1) & less;
+            ci += ((fq >> 1) & 1) & less;
+        }
+        o.uniq[ui] = e;
+        o.ucnt[ui] = cnt;
+        o.uoff[ui] = lt;
+        o.uptr[ui] = addr;
+        if (flag & 2) o.cold[ci] = e;
+    }
+    if (tid == 0) {
+        o.nuniq[0] = nu;
+        o.nuniq[1] = nc;
+        o.status[0] = 0;
+        o.status[1] = nb;
+        o.uoff[nu] = P;
     }
 }
 
 hipError_t launch_select_group_small(const float *z, int T, int k, int renorm, int32_t *ids, float *w,
                                      const GroupArgs &a, char *ws, const WsLayout &L, hipStream_t st) {
-    MOE_LAUNCH("select_group_small", select_group_small, dim3(1), dim3(1024), 0, st, z, T, a.E, k, renorm, ids, w,
-               a.slot, a.n_hot, a.n_cold, a.hot_base, a.scratch, a.blob_bytes, GroupOut::at(ws, L));
+    const GroupOut o = GroupOut::at(ws, L);
+#define MOE_SELECT(N)                                                                                            \
+    MOE_LAUNCH("select_group_small", select_group_small<N>, dim3(1), dim3(1024), 0, st, z, T, a.E, k, renorm, ids, \
+               w, a.slot, a.n_hot, a.n_cold, a.hot_base, a.scratch, a.blob_bytes, o)
+    switch (topk_npl(a.E)) {
+        case 1: MOE_SELECT(1); break;
+        case 2: MOE_SELECT(2); break;
+        case 4: MOE_SELECT(4); break;
+        case 8: MOE_SELECT(8); break;
+        default: MOE_SELECT(16); break;
+    }
+#undef MOE_SELECT
     return hipGetLastError();
 }
 
