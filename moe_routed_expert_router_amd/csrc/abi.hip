@@ -345,6 +345,23 @@ moe_status moe_layer_forward(const moe_shape *s, int32_t T, const uint16_t *x, c
     float *z = reinterpret_cast<float *>(w + L.logits);
     const moe::GroupArgs g = group_args(s, T, topk_ids, r);
     TRY(hip_status(moe::launch_route_logits(x, w_router, bias, T, H, E, z, st), "router logits launch"));
+    if (T <= moe::kSmallRouteTokens && r->n_cold == 0 && moe::ffn_select_fusable(T, k, H, s->inter)) {
+        // no cold expert to gather: the gate/up kernel selects and groups by itself
+        moe::FfnArgs a;
+        a.x = x;
+        a.ids = topk_ids;
+        a.w = topk_w;
+        a.T = T;
+        a.H = H;
+        a.I = s->inter;
+        a.E = E;
+        a.k = k;
+        a.out_bf16 = out_dtype == MOE_OUT_BF16;
+        a.out = out;
+        TRY(hip_status(moe::launch_ffn_select(a, z, renormalize != 0, topk_ids, topk_w, g, w, L, st),
+                       "select + ffn launch"));
+        return ok();
+    }
     if (T <= moe::kSmallRouteTokens) {
         TRY(hip_status(moe::launch_select_group_small(z, T, k, renormalize != 0, topk_ids, topk_w, g, w, L, st),
                        "select-and-group launch"));

@@ -33,6 +33,7 @@
 // this GPU writes the XCD's L2 back each time and costs more than the launch
 // it saves.)
 #include "kernels.hpp"
+#include "select.hpp"
 
 namespace moe {
 
@@ -59,18 +60,13 @@ __device__ __forceinline__ void split_store_h(const f32x4 &g, const f32x4 &u, ui
 // ============================ decode block kernels ==========================
 constexpr int kStageBytes = 49152;   // LDS budget for staged tokens / h rows
 
-// grid (I/16, max distinct experts), 128 * slices threads; LDS: NT rows of x
-// and the per-wave partial sums.
-template <int SPW>
-__global__ __launch_bounds__(512) void ffn_gate_up_blk(const uint16_t *__restrict__ x, int H, int I, int k,
-                                                       int NT, GroupView gv, uint16_t *__restrict__ hhi,
-                                                       uint16_t *__restrict__ hlo) {
-    extern __shared__ __align__(16) char smem[];
-    const int u = blockIdx.y;
-    if (u >= gv.nuniq[0]) return;
-    const uint8_t *base = reinterpret_cast<const uint8_t *>(gv.uptr[u]);
-    if (base == nullptr) return;
-    const int n = gv.ucnt[u], q0 = gv.uoff[u];
+// One (16-row tile, expert) of the decode gate/up: the expert's blob at
+// `base`, its n pairs starting at grouped position q0, pair_of(c) the pair id
+// of its c-th pair.  LDS: NT rows of x and the per-wave partial sums.
+template <int SPW, typename PairOf>
+__device__ __forceinline__ void gate_up_tile_blk(const uint16_t *__restrict__ x, int H, int I, int k, int NT,
+                                                 const uint8_t *base, int n, int q0, PairOf pair_of, char *smem,
+                                                 uint16_t *__restrict__ hhi, uint16_t *__restrict__ hlo) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
     const int nw = blockDim.x >> 6;
     const int role = wave & 1, slice = wave >> 1;   // role 0: gate rows, 1: up rows
@@ -96,7 +92,7 @@ __global__ __launch_bounds__(512) void ffn_gate_up_blk(const uint16_t *__restric
         const int nt = (n - tb) < NT ? (n - tb) : NT;
         __syncthreads();
         for (int c = 0; c < nt; ++c) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)(gv.plist[q0 + tb + c] / k) * H);
+            const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)(pair_of(tb + c) / k) * H);
             for (int j = tid; j < H / 8; j += blockDim.x) xs[c * stride + j] = src[j];
         }
         __syncthreads();
@@ -133,6 +129,39 @@ __global__ __launch_bounds__(512) void ffn_gate_up_blk(const uint16_t *__restric
             }
         }
     }
+}
+
+// grid (I/16, max distinct experts), 128 * slices threads.
+template <int SPW>
+__global__ __launch_bounds__(512) void ffn_gate_up_blk(const uint16_t *__restrict__ x, int H, int I, int k,
+                                                       int NT, GroupView gv, uint16_t *__restrict__ hhi,
+                                                       uint16_t *__restrict__ hlo) {
+    extern __shared__ __align__(16) char smem[];
+    const int u = blockIdx.y;
+    if (u >= gv.nuniq[0]) return;
+    const uint8_t *base = reinterpret_cast<const uint8_t *>(gv.uptr[u]);
+    if (base == nullptr) return;
+    const int q0 = gv.uoff[u];
+    gate_up_tile_blk<SPW>(x, H, I, k, NT, base, gv.ucnt[u], q0, [&](int c) { return gv.plist[q0 + c]; }, smem, hhi,
+                          hlo);
+}
+
+// The same with the top-k and grouping recomputed in every block (no cold
+// expert, T*k <= kFusedSelectPairs): block (0, 0) publishes ids, w and the
+// pick set for the down and combine kernels; block (., u) works on distinct
+// expert u.  grid (I/16, min(E, T*k)), 128 * slices threads.
+template <int SPW, int NPL>
+__global__ __launch_bounds__(512) void ffn_gate_up_sel(const uint16_t *__restrict__ x, int H, int I, int k, int NT,
+                                                       SelectArgs sa, GroupOut o, uint16_t *__restrict__ hhi,
+                                                       uint16_t *__restrict__ hlo) {
+    extern __shared__ __align__(16) char smem[];
+    __shared__ int sid[kFusedSelectPairs], sflag[kFusedSelectPairs], spl[kSmallRouteTokens], sinfo[4];
+    select_group_block<NPL>(sa, o, blockIdx.x == 0 && blockIdx.y == 0, blockIdx.y,
+                            SelectLds{sid, sflag, spl, sinfo});
+    const int n = sinfo[0];
+    const uint8_t *base = reinterpret_cast<const uint8_t *>(((uint64_t)(uint32_t)sinfo[3] << 32) | (uint32_t)sinfo[2]);
+    if (n == 0 || base == nullptr) return;
+    gate_up_tile_blk<SPW>(x, H, I, k, NT, base, n, sinfo[1], [&](int c) { return spl[c]; }, smem, hhi, hlo);
 }
 
 // grid (H/32, max distinct experts), 128 * slices threads; LDS: NT rows of h
@@ -472,6 +501,35 @@ void down_blk(int spw, const FfnArgs &a, const GroupView &gv, const uint16_t *hh
 
 }  // namespace
 
+template <int SPW, int NPL>
+void launch_gate_up_sel(const FfnArgs &a, const SelectArgs &sa, const GroupOut &o, uint16_t *hhi, uint16_t *hlo,
+                        int umax, hipStream_t st) {
+    const int slices = a.H / 128 / SPW;
+    const int row_bytes = (a.H / 8 + 1) * 16;
+    const int NT = stage_rows(row_bytes);
+    const size_t lds = (size_t)NT * row_bytes + (size_t)2 * slices * 64 * 16;
+    MOE_LAUNCH("ffn_gate_up_sel", (ffn_gate_up_sel<SPW, NPL>), dim3(a.I / 16, umax), dim3(128 * slices), lds, st,
+               a.x, a.H, a.I, a.k, NT, sa, o, hhi, hlo);
+}
+
+template <int SPW>
+void gate_up_sel_npl(int npl, const FfnArgs &a, const SelectArgs &sa, const GroupOut &o, uint16_t *hhi,
+                     uint16_t *hlo, int umax, hipStream_t st) {
+    switch (npl) {
+        case 1: launch_gate_up_sel<SPW, 1>(a, sa, o, hhi, hlo, umax, st); break;
+        case 2: launch_gate_up_sel<SPW, 2>(a, sa, o, hhi, hlo, umax, st); break;
+        case 4: launch_gate_up_sel<SPW, 4>(a, sa, o, hhi, hlo, umax, st); break;
+        case 8: launch_gate_up_sel<SPW, 8>(a, sa, o, hhi, hlo, umax, st); break;
+        default: launch_gate_up_sel<SPW, 16>(a, sa, o, hhi, hlo, umax, st); break;
+    }
+}
+
+bool ffn_select_fusable(int T, int k, int H, int I) {
+    if (!ffn_block_path(T, H, I)) return false;
+    const int P = T * k, threads = 128 * (H / 128 / pick_spw(H / 128, 4));
+    return P <= kFusedSelectPairs && P <= threads;
+}
+
 bool ffn_block_path(int T, int H, int I) {
     return T <= 32 && pick_spw(H / 128, 4) != 0 && pick_spw(I / 128, 4) != 0;
 }
@@ -510,6 +568,32 @@ hipError_t launch_ffn(const FfnArgs &a, char *ws, const WsLayout &L, hipStream_t
             MOE_LAUNCH("ffn_down_wave", ffn_down_wave<1>, gd, dim3(64), 0, st, a.H, a.I, gv, hhi, hlo, y);
     }
 
+    const int n4 = a.H / 4;
+    const int ty = a.T < 65535 ? a.T : 65535;
+    MOE_LAUNCH("ffn_combine", ffn_combine, dim3((n4 + 255) / 256, ty), dim3(256), 0, st, y, a.ids, a.w, a.T, a.H,
+               a.E, a.k, a.out_bf16, a.out);
+    return hipGetLastError();
+}
+
+hipError_t launch_ffn_select(const FfnArgs &a, const float *z, int renorm, int32_t *ids, float *w,
+                             const GroupArgs &g, char *ws, const WsLayout &L, hipStream_t st) {
+    const GroupView gv = group_view(ws, L);
+    const GroupOut o = GroupOut::at(ws, L);
+    const SelectArgs sa = select_args(z, a.T, a.k, renorm, ids, w, g);
+    const size_t P = (size_t)a.T * a.k;
+    const int umax = (int)((size_t)a.E < P ? (size_t)a.E : P);
+    uint16_t *hhi = reinterpret_cast<uint16_t *>(ws + L.hbuf);
+    uint16_t *hlo = hhi + P * (size_t)a.I;
+    float *y = reinterpret_cast<float *>(ws + L.ybuf);
+    const int npl = topk_npl(a.E);
+    switch (pick_spw(a.H / 128, 4)) {
+        case 1: gate_up_sel_npl<1>(npl, a, sa, o, hhi, hlo, umax, st); break;
+        case 2: gate_up_sel_npl<2>(npl, a, sa, o, hhi, hlo, umax, st); break;
+        case 4: gate_up_sel_npl<4>(npl, a, sa, o, hhi, hlo, umax, st); break;
+        case 8: gate_up_sel_npl<8>(npl, a, sa, o, hhi, hlo, umax, st); break;
+        default: gate_up_sel_npl<16>(npl, a, sa, o, hhi, hlo, umax, st); break;
+    }
+    down_blk(pick_spw(a.I / 128, 4), a, gv, hhi, hlo, y, umax, st);
     const int n4 = a.H / 4;
     const int ty = a.T < 65535 ? a.T : 65535;
     MOE_LAUNCH("ffn_combine", ffn_combine, dim3((n4 + 255) / 256, ty), dim3(256), 0, st, y, a.ids, a.w, a.T, a.H,

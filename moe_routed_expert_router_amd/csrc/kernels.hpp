@@ -42,6 +42,10 @@ struct GroupArgs {
 };
 hipError_t launch_group(const GroupArgs &a, char *ws, const WsLayout &L, hipStream_t st);
 
+// Arguments of the block-level selection (select.hpp).
+struct SelectArgs;
+SelectArgs select_args(const float *z, int T, int k, int renorm, int32_t *ids, float *w, const GroupArgs &a);
+
 // Decode path (T*k <= 1024): top-k of every token and the whole pick set in
 // one single-block launch.
 hipError_t launch_select_group_small(const float *z, int T, int k, int renorm, int32_t *ids, float *w,
@@ -66,6 +70,17 @@ struct FfnArgs {
     void *out;
 };
 hipError_t launch_ffn(const FfnArgs &a, char *ws, const WsLayout &L, hipStream_t st);
+
+// Decode layer with no cold expert: the gate/up kernel recomputes the top-k
+// and the grouping in every block (block 0 publishes ids, w and the pick set),
+// then down and combine as in launch_ffn.  Needs ffn_select_fusable.
+constexpr int kFusedSelectPairs = 512;
+hipError_t launch_ffn_select(const FfnArgs &a, const float *z, int renorm, int32_t *ids, float *w,
+                             const GroupArgs &g, char *ws, const WsLayout &L, hipStream_t st);
+
+// True when launch_ffn_select applies (block path, T*k within both the
+// selection's LDS and the gate/up block's threads).
+bool ffn_select_fusable(int T, int k, int H, int I);
 
 // True when launch_ffn uses the block kernels (decode sizes).
 bool ffn_block_path(int T, int H, int I);

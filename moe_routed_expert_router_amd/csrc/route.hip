@@ -5,8 +5,8 @@
 // (GB300 inference write-up, mixture-of-experts paragraph).  Scores are a
 // softmax over z[t,e] = x_t . Wr_e + b_e; the k largest logits are kept, equal
 // logits going to the lower expert index, and the kept weights renormalised.
-#include "device_util.hpp"
 #include "kernels.hpp"
+#include "select.hpp"
 
 namespace moe {
 
@@ -214,89 +214,44 @@ hipError_t launch_topk(const float *z, int T, int E, int k, int renorm, int32_t 
     return hipGetLastError();
 }
 
-// Decode path (T * k <= 1024 pairs): top-k of every token (one wave per
-// token) and the whole pick set in one single-block launch.  The grouping is
-// computed from the pair side: pair p of expert e goes to position
-// #{pairs of smaller experts} + #{earlier pairs of e} of the pair list; the
-// first pair of each expert writes its distinct-expert entry (index = number
-// of distinct smaller experts) and, if it is cold, its cold-list entry.
+// Decode path (T * k <= 1024 pairs): top-k of every token and the whole pick
+// set in one single-block launch (the selection itself is shared with the
+// decode gate/up kernel, which recomputes it per block when no expert is cold).
 template <int NPL>
-__global__ __launch_bounds__(1024) void select_group_small(
-    const float *__restrict__ z, int T, int E, int k, int renorm, int32_t *__restrict__ ids,
-    float *__restrict__ w, const int32_t *__restrict__ slot, int n_hot, int n_cold, const uint8_t *hot_base,
-    const uint8_t *scratch, size_t blob_bytes, GroupOut o) {
-    __shared__ int sid[1024];
-    __shared__ int sflag[1024];   // per pair: 1 first of its expert, 2 that expert is cold, 4 unusable
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int t = wave; t < T; t += 16) {
-        int pe;
-        float pw;
-        topk_wave<NPL>(z + (size_t)t * E, E, k, renorm, &pe, &pw);
-        if (lane < k) {
-            ids[(size_t)t * k + lane] = pe;
-            w[(size_t)t * k + lane] = pw;
-            sid[t * k + lane] = pe;
-        }
-    }
-    __syncthreads();
-    const int P = T * k;
-    int e = 0, lt = 0, eqb = 0, cnt = 0, flag = 0;
-    uint64_t addr = 0;
-    if (tid < P) {
-        e = sid[tid];
-        for (int q = 0; q < P; ++q) {
-            const int eq = sid[q];
-            lt += eq < e;
-            cnt += eq == e;
-            eqb += (eq == e) & (q < tid);
-        }
-        if (eqb == 0) {
-            bool ok, cold;
-            addr = expert_address(slot[e], n_hot, n_cold, hot_base, scratch, blob_bytes, &ok, &cold);
-            flag = 1 | ((ok && cold) ? 2 : 0) | (ok ? 0 : 4);
-        }
-        sflag[tid] = flag;
-        o.plist[lt + eqb] = tid;
-    }
-    const int nu = __syncthreads_count(flag & 1);
-    const int nc = __syncthreads_count(flag & 2);
-    const int nb = __syncthreads_count(flag & 4);
-    if (flag & 1) {
-        int ui = 0, ci = 0;
-        for (int q = 0; q < P; ++q) {
-            const int fq = sflag[q], less = sid[q] < e;
-            ui += (fq & 1) & less;
-            ci += ((fq >> 1) & 1) & less;
-        }
-        o.uniq[ui] = e;
-        o.ucnt[ui] = cnt;
-        o.uoff[ui] = lt;
-        o.uptr[ui] = addr;
-        if (flag & 2) o.cold[ci] = e;
-    }
-    if (tid == 0) {
-        o.nuniq[0] = nu;
-        o.nuniq[1] = nc;
-        o.status[0] = 0;
-        o.status[1] = nb;
-        o.uoff[nu] = P;
-    }
+__global__ __launch_bounds__(1024) void select_group_small(SelectArgs a, GroupOut o) {
+    __shared__ int sid[1024], sflag[1024], spl[64], sinfo[4];
+    select_group_block<NPL>(a, o, true, -1, SelectLds{sid, sflag, spl, sinfo});
+}
+
+SelectArgs select_args(const float *z, int T, int k, int renorm, int32_t *ids, float *w, const GroupArgs &a) {
+    SelectArgs s;
+    s.z = z;
+    s.T = T;
+    s.E = a.E;
+    s.k = k;
+    s.renorm = renorm;
+    s.ids = ids;
+    s.w = w;
+    s.slot = a.slot;
+    s.n_hot = a.n_hot;
+    s.n_cold = a.n_cold;
+    s.hot_base = a.hot_base;
+    s.scratch = a.scratch;
+    s.blob_bytes = a.blob_bytes;
+    return s;
 }
 
 hipError_t launch_select_group_small(const float *z, int T, int k, int renorm, int32_t *ids, float *w,
                                      const GroupArgs &a, char *ws, const WsLayout &L, hipStream_t st) {
     const GroupOut o = GroupOut::at(ws, L);
-#define MOE_SELECT(N)                                                                                            \
-    MOE_LAUNCH("select_group_small", select_group_small<N>, dim3(1), dim3(1024), 0, st, z, T, a.E, k, renorm, ids, \
-               w, a.slot, a.n_hot, a.n_cold, a.hot_base, a.scratch, a.blob_bytes, o)
+    const SelectArgs sa = select_args(z, T, k, renorm, ids, w, a);
     switch (topk_npl(a.E)) {
-        case 1: MOE_SELECT(1); break;
-        case 2: MOE_SELECT(2); break;
-        case 4: MOE_SELECT(4); break;
-        case 8: MOE_SELECT(8); break;
-        default: MOE_SELECT(16); break;
+        case 1: MOE_LAUNCH("select_group_small", select_group_small<1>, dim3(1), dim3(1024), 0, st, sa, o); break;
+        case 2: MOE_LAUNCH("select_group_small", select_group_small<2>, dim3(1), dim3(1024), 0, st, sa, o); break;
+        case 4: MOE_LAUNCH("select_group_small", select_group_small<4>, dim3(1), dim3(1024), 0, st, sa, o); break;
+        case 8: MOE_LAUNCH("select_group_small", select_group_small<8>, dim3(1), dim3(1024), 0, st, sa, o); break;
+        default: MOE_LAUNCH("select_group_small", select_group_small<16>, dim3(1), dim3(1024), 0, st, sa, o); break;
     }
-#undef MOE_SELECT
     return hipGetLastError();
 }
 
