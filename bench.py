@@ -160,22 +160,25 @@ def ffn_bytes(w: Workload, picks_per_step: list[np.ndarray]) -> dict:
     """Algorithmic HBM bytes per launch, averaged over the steps' batches:
     each distinct picked expert's planes read once, activations read, results
     written (no re-reads counted)."""
-    L = w.layer
-    H, I, k = L.H, L.I, L.k
-    w13 = 2 * I * (H // 2) + 2 * I * (H // 32)
-    w2 = H * (I // 2) + H * (I // 32)
-    gu, dn, cold_bytes = [], [], []
-    for ids in picks_per_step:
+    return layer_bytes([(w.layer, ids) for ids in picks_per_step])
+
+
+def layer_bytes(layer_picks) -> dict:
+    """As ffn_bytes, over (layer, ids of one launch) pairs (layers may differ)."""
+    gu, dn, cold_bytes, uniq = [], [], [], []
+    for L, ids in layer_picks:
+        H, I, k = L.H, L.I, L.k
+        w13 = 2 * I * (H // 2) + 2 * I * (H // 32)
+        w2 = H * (I // 2) + H * (I // 32)
         U = len(np.unique(ids))
         T = ids.shape[0]
         P = T * k
         gu.append(U * w13 + T * H * 2 + P * I * 4)           # + x read, h (hi+lo) write
         dn.append(U * w2 + P * I * 4 + P * H * 4)            # + h read, y write
-        n_cold = sum(1 for e in np.unique(ids) if L.slot_np[e] < 0)
-        cold_bytes.append(n_cold * L.B)
+        cold_bytes.append(sum(1 for e in np.unique(ids) if L.slot_np[e] < 0) * L.B)
+        uniq.append(U)
     return {"gate_up": float(np.mean(gu)), "down": float(np.mean(dn)),
-            "gather_cold": float(np.mean(cold_bytes)),
-            "unique": float(np.mean([len(np.unique(i)) for i in picks_per_step]))}
+            "gather_cold": float(np.mean(cold_bytes)), "unique": float(np.mean(uniq))}
 
 
 def kernel_role(name: str) -> str | None:
@@ -254,6 +257,82 @@ def measure(name: str, steps: int, warmup: int, reps: int, use_graph: bool, prof
         raise
 
 
+def measure_stack(name: str, steps: int, warmup: int, use_graph: bool) -> dict:
+    """Whole decode steps of a multi-layer workload (every layer in order on
+    one stream, one shared cold scratch); None if it does not fit the GPU."""
+    import torch
+    import moe_routed_expert_router_amd as moe
+    from synth import gen
+    from tests.gpu_setup import Stack
+    wl = gen.workload(name)
+    B = gen.expert_bytes(wl.hidden, wl.inter)
+    need = (wl.layers * wl.hot_count + wl.n_cold) * B
+    free = torch.cuda.mem_get_info()[0]
+    if free < need * 1.05:
+        log(f"[bench] {name}: needs {need / 2**30:.1f} GiB of device memory, {free / 2**30:.1f} free; skipped")
+        return {"skipped": f"needs {need / 2**30:.1f} GiB of device memory, {free / 2**30:.1f} GiB free"}
+    t0 = time.perf_counter()
+    # pinned host memory is capped near 66 GiB on these hosts and the 40 cold pools
+    # need 64.25 GiB: keep headroom, later layers reuse earlier pools
+    S = Stack(wl, log=log, share_host_on_oom=True, max_host_pools=36)
+    log(f"[bench] {name}: {wl.layers} layers resident in {time.perf_counter() - t0:.1f} s")
+    try:
+        for _ in range(warmup):
+            S.forward()
+        torch.cuda.synchronize()
+        graph = None
+        if use_graph:
+            try:
+                s = torch.cuda.Stream()
+                s.wait_stream(torch.cuda.current_stream())
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph, stream=s, capture_error_mode="relaxed"):
+                    S.forward(stream=s)
+                torch.cuda.synchronize()
+                graph.replay()
+                torch.cuda.synchronize()
+            except Exception as e:
+                log(f"[bench] {name}: graph capture failed ({e}); timing eager steps")
+                graph = None
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            if graph is not None:
+                graph.replay()
+            else:
+                S.forward()
+        torch.cuda.synchronize()
+        secs = time.perf_counter() - t0
+        picks = [(L, L.ids.cpu().numpy()) for L in S.layers]
+        moe.moe_profile_reset()
+        moe.moe_profile_enable(True)
+        S.forward()
+        torch.cuda.synchronize()
+        moe.moe_profile_enable(False)
+        stats = moe.moe_profile_read()
+        moe.moe_profile_reset()
+        prof = {k: (n, 1e3 * ms / n) for k, (n, ms) in stats.items() if n}
+        by = layer_bytes(picks)
+        kt = kernel_table(prof, by)
+        ffn_us = prof[role_kernel(prof, "gate_up")][1] + prof[role_kernel(prof, "down")][1] + \
+            prof.get("ffn_combine", (0, 0.0))[1]
+        entry = {"tokens_per_s": round(steps * wl.tokens / secs, 2), "ms_per_step": round(1e3 * secs / steps, 4),
+                 "layers": wl.layers, "tokens_per_layer": wl.tokens, "steps": steps, "graph": graph is not None,
+                 "distinct_cold_pools": S.distinct_host_pools,
+                 "mean_distinct_experts_per_layer": round(by["unique"], 2),
+                 "ffn_hbm_GB_per_s": round((by["gate_up"] + by["down"]) / (ffn_us * 1e-6) / 1e9, 1),
+                 "kernels_per_layer": kt}
+        if "gather_cold" in prof and by["gather_cold"] > 0:
+            entry["gather_link_GB_per_s"] = round(by["gather_cold"] / (prof["gather_cold"][1] * 1e-6) / 1e9, 2)
+            entry["gather_bytes_per_layer"] = int(by["gather_cold"])
+        log(f"[bench] {name}: {entry['ms_per_step']:.3f} ms/step, {entry['tokens_per_s']} tokens/s")
+        return entry
+    finally:
+        S.close()
+        del S
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -265,6 +344,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batch8", action="store_true", help="skip the batch-8 hot/cold secondary figures")
+    ap.add_argument("--no-step40", action="store_true", help="skip the 40-layer batch-32 secondary figures")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="first run one plain float64 copy of this many MiB (a known-size kernel for "
                          "scaling hardware byte counters)")
@@ -330,6 +410,10 @@ def main():
         w8.close()
         del w8
         torch.cuda.empty_cache()
+
+    if not a.no_step40 and a.workload == "decode1":
+        log("[bench] secondary: step40 (40 layers, batch 32, 255 hot / 129 cold, shared scratch)")
+        extra["step40_batch32"] = measure_stack("step40", 10, 2, not a.no_graph)
 
     cpu = None
     if not a.no_cpu_baseline:

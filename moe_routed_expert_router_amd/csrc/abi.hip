@@ -109,7 +109,10 @@ moe_status check_residency(const moe_shape *s, const moe_residency *r) {
 }
 
 moe_status hip_status(hipError_t e, const char *what) {
-    if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    if (e != hipSuccess) {
+        (void)hipGetLastError();   // reported here: do not leave it for the caller's next HIP call
+        return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    }
     return MOE_OK;
 }
 

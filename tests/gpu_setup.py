@@ -51,7 +51,7 @@ class Layer:
 
     def __init__(self, wl: gen.Workload, layer: int = 0, T: int | None = None, scratch=None,
                  all_hot: bool = False, cal: dict | None = None, coherent: bool = False,
-                 hot: list | None = None):
+                 hot: list | None = None, host: HostBuffer | None = None):
         self.wl, self.layer = wl, layer
         H, I, E, k = wl.hidden, wl.inter, wl.n_experts, wl.top_k
         self.H, self.I, self.E, self.k = H, I, E, k
@@ -85,10 +85,15 @@ class Layer:
         if self.n_hot:
             gen.fill_expert_blobs_device(self.hot_base, seed, layer, self.hot, H, I)
         self.host = None
+        self.own_host = host is None   # a borrowed pool keeps another layer's bytes
         self.scratch = None
         if self.n_cold:
-            self.host = HostBuffer(self.n_cold * self.B, coherent)
-            fill_host_experts(self.host, seed, layer, self.cold, H, I)
+            if host is None:
+                self.host = HostBuffer(self.n_cold * self.B, coherent)
+                fill_host_experts(self.host, seed, layer, self.cold, H, I)
+            else:
+                assert host.nbytes == self.n_cold * self.B
+                self.host = host
             self.scratch = scratch if scratch is not None else torch.empty(
                 (self.n_cold, self.B), dtype=torch.uint8, device=dev)
         self.residency = moe.residency(self.slot, self.hot_base if self.n_hot else None,
@@ -110,6 +115,53 @@ class Layer:
         return out
 
     def close(self):
-        if self.host:
+        if self.host and self.own_host:
             self.host.close()
-            self.host = None
+        self.host = None
+
+
+class Stack:
+    """`layers` sequential layers of a workload (each with its own seeded
+    tokens, router, Zipf prior, hot pool and pinned cold pool) sharing one
+    cold scratch, run in order on one stream.  Tokens are independent per
+    layer (an unnormalised synthetic layer's output is not a usable input)."""
+
+    def __init__(self, wl: gen.Workload, layers: int | None = None, T: int | None = None, log=None,
+                 share_host_on_oom: bool = False, max_host_pools: int | None = None):
+        cal = gen.load_calibration() if wl.zipf else None
+        n = wl.layers if layers is None else layers
+        B = gen.expert_bytes(wl.hidden, wl.inter)
+        self.scratch = torch.empty((max(wl.n_cold, 1), B), dtype=torch.uint8, device="cuda")
+        self.layers = []
+        self.distinct_host_pools = 0
+        try:
+            for l in range(n):
+                L = None
+                if max_host_pools is None or self.distinct_host_pools < max_host_pools:
+                    try:
+                        L = Layer(wl, layer=l, T=T, scratch=self.scratch, cal=cal)
+                    except moe.MoeError:
+                        if not share_host_on_oom or not self.distinct_host_pools:
+                            raise
+                if L is None:
+                    # no (more) pinned host memory: reuse an earlier layer's cold pool
+                    # (same host-link traffic; that layer's bytes, not this one's)
+                    donor = self.layers[l % self.distinct_host_pools]
+                    L = Layer(wl, layer=l, T=T, scratch=self.scratch, cal=cal, host=donor.host)
+                self.distinct_host_pools += int(L.own_host)
+                self.layers.append(L)
+                if log and (l % 10 == 9 or l == n - 1):
+                    log(f"[setup] {l + 1}/{n} layers resident, {self.distinct_host_pools} distinct cold pools")
+        except Exception:
+            self.close()
+            raise
+        self.wl = wl
+
+    def forward(self, stream=None):
+        for L in self.layers:
+            L.forward(stream=stream)
+
+    def close(self):
+        for L in self.layers:
+            L.close()
+        self.layers = []

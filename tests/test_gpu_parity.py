@@ -28,7 +28,7 @@ from oracle import gather as ogather  # noqa: E402
 from oracle import layer as olayer  # noqa: E402
 from oracle import route as oroute  # noqa: E402
 from synth import gen  # noqa: E402
-from tests.gpu_setup import Layer  # noqa: E402
+from tests.gpu_setup import Layer, Stack  # noqa: E402
 
 TOL = 2e-2
 TIGHT = 1e-3
@@ -263,6 +263,57 @@ def test_wave_path_for_unaligned_hidden():
     ref = oracle_out(L)
     assert np.array_equal(L.ids.cpu().numpy(), ref["ids"])
     check_out(out.cpu().numpy(), ref["out"])
+
+
+@pytest.mark.timeout(900)
+def test_step40_full_size():
+    """The 40-layer decode step at full size: 40 x (255 hot in HBM, 129 cold in
+    pinned host memory), one shared 129-slot scratch, batch 32, run in layer
+    order on one stream.  Checks: routing of every layer (R1-R3 against the
+    oracle); outputs of sampled layers and tokens; and the shared scratch after
+    the step - each slot holds the bytes of the last layer that picked the
+    cold expert mapped to it, and a slot no layer picked is untouched."""
+    wl = gen.workload("step40")
+    B = gen.expert_bytes(wl.hidden, wl.inter)
+    need = (wl.layers * wl.n_hot + wl.n_cold) * B
+    if torch.cuda.mem_get_info()[0] < need * 1.05:
+        pytest.skip("not enough device memory for the 40-layer step")
+    try:
+        S = Stack(wl)
+    except moe.MoeError as e:
+        pytest.skip(f"pinned host memory for the 40 cold pools is not available here ({e})")
+    try:
+        S.scratch.fill_(0xEE)
+        S.forward()
+        torch.cuda.synchronize()
+        picks = []
+        for L in S.layers:
+            ids_g, w_g, z_g = route_on_gpu(L)
+            assert np.array_equal(L.ids.cpu().numpy(), ids_g)
+            check_route(L, ids_g, w_g, z_g)
+            picks.append(ids_g)
+        rows = np.array([0, 31])
+        for li in (0, 39):
+            L = S.layers[li]
+            ref = oracle_out(L, rows)
+            check_out(L.out.cpu().numpy()[rows], ref["out"])
+        # shared scratch: last writer per slot
+        scratch = S.scratch.cpu().numpy()
+        last = {}
+        for li, L in enumerate(S.layers):
+            for e in ogather.picked_cold(picks[li], L.slot_np):
+                last[-int(L.slot_np[e]) - 1] = li
+        for cs in range(wl.n_cold):
+            if cs in last:
+                L = S.layers[last[cs]]
+                assert np.array_equal(scratch[cs], L.host.np[cs * B:(cs + 1) * B]), (cs, last[cs])
+            else:
+                assert np.all(scratch[cs] == 0xEE), cs
+        n_cold = [len(ogather.picked_cold(p, L.slot_np)) for p, L in zip(picks, S.layers)]
+        print(f"step40: distinct experts per layer {np.mean([len(np.unique(p)) for p in picks]):.1f}, "
+              f"picked cold per layer {np.mean(n_cold):.2f}, scratch slots written {len(last)}")
+    finally:
+        S.close()
 
 
 def test_max_experts_and_k():
