@@ -189,23 +189,41 @@ def kernel_role(name: str) -> str | None:
         return "down"
     if name == "gather_cold":
         return "gather_cold"
+    if name == "ffn_combine":
+        return "combine"
     return None
 
 
+def forwards(prof: dict) -> int:
+    """Layer forwards covered by a profile (every forward runs one router-logits kernel)."""
+    return max(n for k, (n, _) in prof.items() if k.startswith("route_logits"))
+
+
+def role_us(prof: dict, role: str) -> float:
+    """Microseconds per layer forward spent in the kernels of one role (a role
+    may run as several launches, e.g. the hot and the cold part of the FFN)."""
+    per = forwards(prof)
+    return sum(n * us for k, (n, us) in prof.items() if kernel_role(k) == role) / per
+
+
 def kernel_table(prof: dict, by: dict) -> dict:
+    """Per kernel: launches, mean duration and microseconds per layer forward;
+    per FFN role: algorithmic bytes per forward over that role's time."""
+    per = forwards(prof)
     out = {}
     for k, (n, us) in sorted(prof.items()):
-        e = {"launches": n, "mean_us": round(us, 3)}
-        role = kernel_role(k)
-        if role and by.get(role):
-            e["algorithmic_bytes"] = int(by[role])
-            e["GB_per_s"] = round(by[role] / (us * 1e-6) / 1e9, 1)
-        out[k] = e
+        out[k] = {"launches": n, "mean_us": round(us, 3), "us_per_forward": round(n * us / per, 3)}
+    for role in ("gate_up", "down", "gather_cold"):
+        t = role_us(prof, role)
+        if t > 0 and by.get(role):
+            out[f"role:{role}"] = {"us_per_forward": round(t, 3), "algorithmic_bytes": int(by[role]),
+                                   "GB_per_s": round(by[role] / (t * 1e-6) / 1e9, 1)}
     return out
 
 
 def role_kernel(prof: dict, role: str) -> str:
-    return next(k for k in prof if kernel_role(k) == role)
+    """The kernel of a role with the most time per forward."""
+    return max((k for k in prof if kernel_role(k) == role), key=lambda k: prof[k][0] * prof[k][1])
 
 
 def cpu_baseline(name: str, seconds: float) -> dict:
@@ -255,6 +273,58 @@ def measure(name: str, steps: int, warmup: int, reps: int, use_graph: bool, prof
     except Exception:
         w.close()
         raise
+
+
+def measure_ffn_batches(batches=(1, 8, 32), layers: int = 4, reps: int = 10) -> dict:
+    """The grouped FFN alone (moe_expert_ffn over every expert resident) at
+    decode batch sizes, routed with the 40-layer workload's Zipf prior;
+    `layers` independent layers rotate so that successive launches read
+    different experts.  Kernel durations from the library's launch events."""
+    import torch
+    import moe_routed_expert_router_amd as moe
+    from synth import gen
+    from tests.gpu_setup import Layer
+    wl = gen.workload("step40")
+    out = {}
+    for T in batches:
+        Ls = [Layer(wl, layer=l, T=T, all_hot=True) for l in range(layers)]
+        try:
+            for L in Ls:
+                L.forward()
+            torch.cuda.synchronize()
+            picks = [(L, L.ids.cpu().numpy()) for L in Ls]
+            for it in range(2):   # one untimed round, then the profiled one
+                if it:
+                    moe.moe_profile_reset()
+                    moe.moe_profile_enable(True)
+                for _ in range(reps):
+                    for L in Ls:
+                        moe.moe_expert_ffn(L.shape, L.x, L.ids, L.w, L.residency, L.out, L.ws)
+                torch.cuda.synchronize()
+            moe.moe_profile_enable(False)
+            raw = moe.moe_profile_read()
+            moe.moe_profile_reset()
+            prof = {k: (n, 1e3 * ms / n) for k, (n, ms) in raw.items() if n}
+            per = layers * reps
+            us = {r: sum(n * u for k, (n, u) in prof.items() if kernel_role(k) == r) / per
+                  for r in ("gate_up", "down", "combine")}
+            by = layer_bytes(picks)
+            ffn_us = us["gate_up"] + us["down"] + us["combine"]
+            gbs = (by["gate_up"] + by["down"]) / (ffn_us * 1e-6) / 1e9
+            out[f"batch{T}"] = {
+                "tokens": T, "mean_distinct_experts": round(by["unique"], 2),
+                "gate_up_us": round(us["gate_up"], 3), "down_us": round(us["down"], 3),
+                "combine_us": round(us["combine"], 3),
+                "gate_up_GB_per_s": round(by["gate_up"] / (us["gate_up"] * 1e-6) / 1e9, 1),
+                "down_GB_per_s": round(by["down"] / (us["down"] * 1e-6) / 1e9, 1),
+                "ffn_hbm_GB_per_s": round(gbs, 1), "ffn_frac": round(gbs / HBM_PEAK_GBS, 4)}
+            log(f"[bench] ffn batch {T}: {ffn_us:.1f} us, {gbs:.0f} GB/s")
+        finally:
+            for L in Ls:
+                L.close()
+            del Ls
+            torch.cuda.empty_cache()
+    return out
 
 
 def measure_stack(name: str, steps: int, warmup: int, use_graph: bool) -> dict:
@@ -314,8 +384,7 @@ def measure_stack(name: str, steps: int, warmup: int, use_graph: bool) -> dict:
         prof = {k: (n, 1e3 * ms / n) for k, (n, ms) in stats.items() if n}
         by = layer_bytes(picks)
         kt = kernel_table(prof, by)
-        ffn_us = prof[role_kernel(prof, "gate_up")][1] + prof[role_kernel(prof, "down")][1] + \
-            prof.get("ffn_combine", (0, 0.0))[1]
+        ffn_us = role_us(prof, "gate_up") + role_us(prof, "down") + role_us(prof, "combine")
         entry = {"tokens_per_s": round(steps * wl.tokens / secs, 2), "ms_per_step": round(1e3 * secs / steps, 4),
                  "layers": wl.layers, "tokens_per_layer": wl.tokens, "steps": steps, "graph": graph is not None,
                  "distinct_cold_pools": S.distinct_host_pools,
@@ -323,7 +392,7 @@ def measure_stack(name: str, steps: int, warmup: int, use_graph: bool) -> dict:
                  "ffn_hbm_GB_per_s": round((by["gate_up"] + by["down"]) / (ffn_us * 1e-6) / 1e9, 1),
                  "kernels_per_layer": kt}
         if "gather_cold" in prof and by["gather_cold"] > 0:
-            entry["gather_link_GB_per_s"] = round(by["gather_cold"] / (prof["gather_cold"][1] * 1e-6) / 1e9, 2)
+            entry["gather_link_GB_per_s"] = round(by["gather_cold"] / (role_us(prof, "gather_cold") * 1e-6) / 1e9, 2)
             entry["gather_bytes_per_layer"] = int(by["gather_cold"])
         log(f"[bench] {name}: {entry['ms_per_step']:.3f} ms/step, {entry['tokens_per_s']} tokens/s")
         return entry
@@ -344,6 +413,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batch8", action="store_true", help="skip the batch-8 hot/cold secondary figures")
+    ap.add_argument("--no-ffn-batches", action="store_true",
+                    help="skip the standalone grouped-FFN figures at batch 1/8/32")
     ap.add_argument("--no-step40", action="store_true", help="skip the 40-layer batch-32 secondary figures")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="first run one plain float64 copy of this many MiB (a known-size kernel for "
@@ -380,13 +451,14 @@ def main():
     log(f"[bench] {steps} steps in {secs:.4f} s ({ms_per_step * 1e3:.1f} us/step), graph={graphed}")
     kernels = kernel_table(prof, by)
     for k, e in kernels.items():
-        log(f"[bench]   {k:24s} {e['mean_us']:9.2f} us" + (f"  {e['GB_per_s']:8.1f} GB/s" if "GB_per_s" in e else ""))
+        log(f"[bench]   {k:24s} {e['us_per_forward']:9.2f} us/forward" +
+            (f"  {e['GB_per_s']:8.1f} GB/s" if "GB_per_s" in e else ""))
     dom = role_kernel(prof, "gate_up")
     dn = role_kernel(prof, "down")
     dom_us = prof[dom][1]
     achieved = by["gate_up"] / (dom_us * 1e-6) / 1e9
     traffic = read_traffic(dom, a.workload)
-    ffn_us = dom_us + prof[dn][1] + prof.get("ffn_combine", (0, 0.0))[1]
+    ffn_us = role_us(prof, "gate_up") + role_us(prof, "down") + role_us(prof, "combine")
     ffn_gbs = (by["gate_up"] + by["down"]) / (ffn_us * 1e-6) / 1e9
     w.close()
     del w
@@ -397,19 +469,22 @@ def main():
         log("[bench] secondary: hotcold8 (batch 8, 255 hot / 129 cold)")
         w8, s8, st8, g8, p8, b8 = measure("hotcold8", 128, 8, 16, not a.no_graph, 64)
         k8 = kernel_table(p8, b8)
-        ffn8_us = p8[role_kernel(p8, "gate_up")][1] + p8[role_kernel(p8, "down")][1] + \
-            p8.get("ffn_combine", (0, 0.0))[1]
+        ffn8_us = role_us(p8, "gate_up") + role_us(p8, "down") + role_us(p8, "combine")
         entry = {"tokens_per_s": round(st8 * 8 / s8, 1), "ms_per_step": round(1e3 * s8 / st8, 4),
                  "graph": g8, "mean_distinct_experts": round(b8["unique"], 2),
                  "ffn_hbm_GB_per_s": round((b8["gate_up"] + b8["down"]) / (ffn8_us * 1e-6) / 1e9, 1),
                  "kernels": k8}
         if "gather_cold" in p8 and b8["gather_cold"] > 0:
-            entry["gather_link_GB_per_s"] = round(b8["gather_cold"] / (p8["gather_cold"][1] * 1e-6) / 1e9, 2)
+            entry["gather_link_GB_per_s"] = round(b8["gather_cold"] / (role_us(p8, "gather_cold") * 1e-6) / 1e9, 2)
             entry["gather_bytes_per_step"] = int(b8["gather_cold"])
         extra["batch8_hotcold"] = entry
         w8.close()
         del w8
         torch.cuda.empty_cache()
+
+    if not a.no_ffn_batches and a.workload == "decode1":
+        log("[bench] secondary: grouped FFN alone at batch 1/8/32 (all experts resident)")
+        extra["ffn_by_batch"] = measure_ffn_batches()
 
     if not a.no_step40 and a.workload == "decode1":
         log("[bench] secondary: step40 (40 layers, batch 32, 255 hot / 129 cold, shared scratch)")

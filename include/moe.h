@@ -180,8 +180,14 @@ moe_status moe_expert_ffn(const moe_shape *s, int32_t n_tokens, const uint16_t *
                           void *ws, size_t ws_bytes, void *stream);
 
 /* The whole layer: moe_route, then the pick set, the cold gather
- * (skipped when r->n_cold == 0) and the grouped FFN with the combine, all on
- * `stream`.  topk_ids / topk_w receive the routing. */
+ * (skipped when r->n_cold == 0) and the grouped FFN with the combine, ordered
+ * on `stream`: the call returns with everything enqueued after work already
+ * on `stream` and later work on `stream` sees the finished layer.  At decode
+ * sizes with cold experts, the gather runs on a library-owned side stream of
+ * the current device (default priority, created on first use) forked from and
+ * joined back into `stream` by events, while the hot experts' FFN runs on
+ * `stream`; the pattern is valid under stream capture.  topk_ids / topk_w
+ * receive the routing. */
 moe_status moe_layer_forward(const moe_shape *s, int32_t n_tokens, const uint16_t *x,
                              const float *w_router, const float *bias, int32_t renormalize,
                              const moe_residency *r, int32_t *topk_ids, float *topk_w,

@@ -9,6 +9,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kernels.hpp"
 
 namespace {
@@ -145,6 +147,47 @@ moe_status enqueue_ffn(const moe_shape *s, int32_t T, const uint16_t *x, const i
     a.out_bf16 = out_dtype == MOE_OUT_BF16;
     a.out = out;
     return hip_status(moe::launch_ffn(a, ws, L, st), "ffn launch");
+}
+
+// Per-device side stream on which moe_layer_forward runs the cold gather while
+// the hot experts' FFN runs on the caller's stream.  Created on first use with
+// the default priority; the fork and join are event waits, so the pattern is
+// also valid under stream capture.  The mutex keeps one call's record/wait
+// pairs together when several host threads drive the same device.
+struct SideStream {
+    std::mutex mu;
+    hipStream_t st = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+SideStream g_side[kMaxDevices];
+
+moe_status side_stream(std::unique_lock<std::mutex> &lock, SideStream **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return fail(MOE_ERR_HIP, "no usable current device for the gather stream");
+    }
+    SideStream &s = g_side[dev];
+    lock = std::unique_lock<std::mutex>(s.mu);
+    if (s.st == nullptr) {
+        hipStream_t st = nullptr;
+        hipEvent_t a = nullptr, b = nullptr;
+        if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess ||
+            hipEventCreateWithFlags(&a, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&b, hipEventDisableTiming) != hipSuccess) {
+            const hipError_t e = hipGetLastError();
+            if (b) (void)hipEventDestroy(b);
+            if (a) (void)hipEventDestroy(a);
+            if (st) (void)hipStreamDestroy(st);
+            return fail(MOE_ERR_HIP, "gather stream setup: %s", hipGetErrorString(e));
+        }
+        s.st = st;
+        s.fork = a;
+        s.join = b;
+    }
+    *out = &s;
+    return MOE_OK;
 }
 
 moe_status check_out(const moe_shape *s, int32_t T, int32_t out_dtype, void *out) {
@@ -371,6 +414,37 @@ moe_status moe_layer_forward(const moe_shape *s, int32_t T, const uint16_t *x, c
     } else {
         TRY(hip_status(moe::launch_topk(z, T, E, k, renormalize != 0, topk_ids, topk_w, st), "top-k launch"));
         TRY(hip_status(moe::launch_group(g, w, L, st), "pick-set launch"));
+    }
+    if (r->n_cold > 0 && moe::ffn_block_path(T, H, s->inter)) {
+        // the hot experts' FFN needs nothing from the gather: it runs on the
+        // caller's stream while the side stream copies the cold experts in;
+        // the cold experts' FFN and the combine follow the join
+        moe::FfnArgs a;
+        a.x = x;
+        a.ids = topk_ids;
+        a.w = topk_w;
+        a.T = T;
+        a.H = H;
+        a.I = s->inter;
+        a.E = E;
+        a.k = k;
+        a.out_bf16 = out_dtype == MOE_OUT_BF16;
+        a.out = out;
+        const int P = T * k;
+        std::unique_lock<std::mutex> lock;
+        SideStream *side = nullptr;
+        TRY(side_stream(lock, &side));
+        TRY(hip_status(hipEventRecord(side->fork, st), "gather fork"));
+        TRY(hip_status(hipStreamWaitEvent(side->st, side->fork, 0), "gather fork"));
+        TRY(hip_status(moe::launch_gather(r->host_cold, r->scratch, g.blob_bytes, r->slot, w, L, side->st),
+                       "gather launch"));
+        TRY(hip_status(hipEventRecord(side->join, side->st), "gather join"));
+        TRY(hip_status(moe::launch_ffn_part(a, moe::kPartHot, E < P ? E : P, w, L, st), "hot ffn launch"));
+        TRY(hip_status(hipStreamWaitEvent(st, side->join, 0), "gather join"));
+        lock.unlock();
+        TRY(hip_status(moe::launch_ffn_part(a, moe::kPartCold, r->n_cold < P ? r->n_cold : P, w, L, st),
+                       "cold ffn launch"));
+        return ok();
     }
     if (r->n_cold > 0)
         TRY(hip_status(moe::launch_gather(r->host_cold, r->scratch, g.blob_bytes, r->slot, w, L, st),

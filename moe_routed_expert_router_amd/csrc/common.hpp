@@ -49,6 +49,8 @@ struct WsLayout {
     size_t uoff;       // int32 [E+1]: start of each expert's run in plist
     size_t uptr;       // uint64 [E]: blob address of each distinct expert (0: skip)
     size_t cold;       // int32 [E]: picked cold experts, increasing
+    size_t ucold;      // int32 [E]: 1 if distinct expert u reads a scratch slot, else 0
+    size_t cu;         // int32 [E]: distinct-expert index of each picked cold expert
     size_t counts;     // int32 [E]: pairs per expert id
     size_t hist;       // int32 [nchunks][E+1]: per-chunk counts (+ bad ids), then chunk bases
     size_t rank;       // int32 [P]: rank of a pair among its chunk's pairs of that expert
@@ -85,6 +87,8 @@ struct WsLayout {
         w.uoff = take((size_t)(E + 1) * 4);
         w.uptr = take((size_t)E * 8);
         w.cold = take((size_t)E * 4);
+        w.ucold = take((size_t)E * 4);
+        w.cu = take((size_t)E * 4);
         w.counts = take((size_t)E * 4);
         w.hist = take((size_t)w.nchunks * (E + 1) * 4);
         w.rank = take(P * 4);
@@ -107,12 +111,14 @@ struct GroupView {
     const uint64_t *uptr;
     const int32_t *plist;
     const int32_t *cold;
+    const int32_t *ucold;
+    const int32_t *cu;
     const int32_t *tlist;
 };
 
 // Mutable view of the grouping outputs, for the kernels that write them.
 struct GroupOut {
-    int32_t *sync, *status, *counts, *nuniq, *uniq, *ucnt, *uoff, *cold, *plist, *tlist;
+    int32_t *sync, *status, *counts, *nuniq, *uniq, *ucnt, *uoff, *cold, *ucold, *cu, *plist, *tlist;
     uint64_t *uptr;
     static GroupOut at(char *ws, const WsLayout &L) {
         GroupOut o;
@@ -124,6 +130,8 @@ struct GroupOut {
         o.ucnt = reinterpret_cast<int32_t *>(ws + L.ucnt);
         o.uoff = reinterpret_cast<int32_t *>(ws + L.uoff);
         o.cold = reinterpret_cast<int32_t *>(ws + L.cold);
+        o.ucold = reinterpret_cast<int32_t *>(ws + L.ucold);
+        o.cu = reinterpret_cast<int32_t *>(ws + L.cu);
         o.plist = reinterpret_cast<int32_t *>(ws + L.plist);
         o.tlist = reinterpret_cast<int32_t *>(ws + L.tlist);
         o.uptr = reinterpret_cast<uint64_t *>(ws + L.uptr);
@@ -141,6 +149,8 @@ inline GroupView group_view(char *ws, const WsLayout &L) {
     v.uptr = reinterpret_cast<const uint64_t *>(ws + L.uptr);
     v.plist = reinterpret_cast<const int32_t *>(ws + L.plist);
     v.cold = reinterpret_cast<const int32_t *>(ws + L.cold);
+    v.ucold = reinterpret_cast<const int32_t *>(ws + L.ucold);
+    v.cu = reinterpret_cast<const int32_t *>(ws + L.cu);
     v.tlist = reinterpret_cast<const int32_t *>(ws + L.tlist);
     return v;
 }

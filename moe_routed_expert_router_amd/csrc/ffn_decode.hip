@@ -17,15 +17,20 @@
 // only per-element vector work (about a fifth of the issue slots at the HBM
 // rate), and 1 to 16 tokens per expert cost the same.
 //
-// Decode kernels (T <= 32), one 512-thread block per (row tile, expert):
-//   gate/up: 8 waves = {gate, up} x 4 K slices; each wave issues all of its
+// Decode kernels (T <= 32), one 512-thread block per (row block, expert):
+//   gate/up: 8 waves = {gate, up} x RT row tiles x K slices (RT = 1 below 8
+//            tokens, 2 from 8 tokens on, so that one staging of the token
+//            rows serves twice the weight rows); each wave issues all of its
 //            slice's weight loads at once (memory-level parallelism comes
 //            from many small independent waves, not deep per-wave pipelines);
 //            tokens are staged once per block in LDS; the slice partials are
 //            added in a fixed order in LDS; h = silu(g) * u is stored as bf16
 //            hi + lo parts (h - hi rounded again), ~16 significant bits.
-//   down:    8 waves = 2 row tiles x 4 K slices over a 32-row block, B = h hi
-//            and h lo (two MFMAs per K slice), y[pair][row] in fp32.
+//   down:    8 waves = RT row tiles x K slices (RT = 2 below 8 tokens, else
+//            4 with the first h units requested ahead of the weights), B = h
+//            hi and h lo (two MFMAs per K slice), y[pair][row] in fp32.
+// The block shapes depend only on T and the layer shape, never on where the
+// experts live, so all-resident and mixed runs still add in the same order.
 // General kernels (any T): one wave per 16 rows.
 // Both end with the combine kernel: out[t] = sum_j w[t,j] * y[t*k+j] in j
 // order, no float atomics.  (Folding the combine into the down kernel through
@@ -59,20 +64,33 @@ __device__ __forceinline__ void split_store_h(const f32x4 &g, const f32x4 &u, ui
 
 // ============================ decode block kernels ==========================
 constexpr int kStageBytes = 49152;   // LDS budget for staged tokens / h rows
+constexpr int kWideTokens = 8;       // tokens from which blocks take more weight rows
 
-// One (16-row tile, expert) of the decode gate/up: the expert's blob at
+// Distinct expert of this block for an FFN part (FfnPart), or -1 when the
+// block has none: every distinct expert belongs to exactly one of the hot and
+// cold parts, so the hot and cold launches together equal one kPartAll launch.
+__device__ __forceinline__ int part_expert(const GroupView &gv, int part) {
+    const int b = blockIdx.y;
+    if (part == kPartCold) return b < gv.nuniq[1] ? gv.cu[b] : -1;
+    if (b >= gv.nuniq[0]) return -1;
+    return (part == kPartHot && gv.ucold[b]) ? -1 : b;
+}
+
+// RT 16-row tiles of one expert in the decode gate/up: the expert's blob at
 // `base`, its n pairs starting at grouped position q0, pair_of(c) the pair id
-// of its c-th pair.  LDS: NT rows of x and the per-wave partial sums.
+// of its c-th pair.  Waves: {gate, up} x RT tiles x K slices.  LDS: NT rows of
+// x (staged once for all RT tiles) and the per-wave partial sums.
 template <int SPW, typename PairOf>
 __device__ __forceinline__ void gate_up_tile_blk(const uint16_t *__restrict__ x, int H, int I, int k, int NT,
-                                                 const uint8_t *base, int n, int q0, PairOf pair_of, char *smem,
+                                                 int RT, const uint8_t *base, int n, int q0, PairOf pair_of, char *smem,
                                                  uint16_t *__restrict__ hhi, uint16_t *__restrict__ hlo) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
     const int nw = blockDim.x >> 6;
-    const int role = wave & 1, slice = wave >> 1;   // role 0: gate rows, 1: up rows
-    const int rt = blockIdx.x;
+    const int role = wave & 1;   // role 0: gate rows, 1: up rows
+    const int rt = (wave >> 1) % RT, slice = (wave >> 1) / RT;
+    const int col0 = blockIdx.x * 16 * RT + rt * 16;   // first h column of this wave's tile
     const BlobLayout L = BlobLayout::make(H, I);
-    const size_t row = (size_t)role * I + (size_t)rt * 16 + r;
+    const size_t row = (size_t)role * I + col0 + r;
     const uint8_t *qp = base + L.w13_codes + row * (H / 2) + (size_t)slice * SPW * 64 + 16 * g;
     const uint8_t *sp = base + L.w13_scales + row * (H / 32) + (size_t)slice * SPW * 4;
 
@@ -117,42 +135,42 @@ __device__ __forceinline__ void gate_up_tile_blk(const uint16_t *__restrict__ x,
         }
         red[wave * 64 + lane] = acc;
         __syncthreads();
-        if (wave == 0) {
-            f32x4 gs = red[lane], us = red[64 + lane];
-            for (int w = 2; w < nw; w += 2) {   // slices in a fixed order
+        if (role == 0 && slice == 0) {   // the tile's gate wave adds its slices in a fixed order
+            f32x4 gs = red[wave * 64 + lane], us = red[(wave + 1) * 64 + lane];
+            for (int w = wave + 2 * RT; w < nw; w += 2 * RT) {
                 gs += red[w * 64 + lane];
                 us += red[(w + 1) * 64 + lane];
             }
             if (tv) {
-                const size_t off = (size_t)(q0 + tb + r) * I + (size_t)rt * 16 + 4 * g;
+                const size_t off = (size_t)(q0 + tb + r) * I + col0 + 4 * g;
                 split_store_h(gs, us, hhi + off, hlo + off);
             }
         }
     }
 }
 
-// grid (I/16, max distinct experts), 128 * slices threads.
+// grid (I/(16*RT), max distinct experts of the part), 128 * RT * slices threads.
 template <int SPW>
 __global__ __launch_bounds__(512) void ffn_gate_up_blk(const uint16_t *__restrict__ x, int H, int I, int k,
-                                                       int NT, GroupView gv, uint16_t *__restrict__ hhi,
+                                                       int NT, int RT, GroupView gv, int part, uint16_t *__restrict__ hhi,
                                                        uint16_t *__restrict__ hlo) {
     extern __shared__ __align__(16) char smem[];
-    const int u = blockIdx.y;
-    if (u >= gv.nuniq[0]) return;
+    const int u = part_expert(gv, part);
+    if (u < 0) return;
     const uint8_t *base = reinterpret_cast<const uint8_t *>(gv.uptr[u]);
     if (base == nullptr) return;
     const int q0 = gv.uoff[u];
-    gate_up_tile_blk<SPW>(x, H, I, k, NT, base, gv.ucnt[u], q0, [&](int c) { return gv.plist[q0 + c]; }, smem, hhi,
-                          hlo);
+    gate_up_tile_blk<SPW>(x, H, I, k, NT, RT, base, gv.ucnt[u], q0, [&](int c) { return gv.plist[q0 + c]; }, smem,
+                          hhi, hlo);
 }
 
 // The same with the top-k and grouping recomputed in every block (no cold
 // expert, T*k <= kFusedSelectPairs): block (0, 0) publishes ids, w and the
 // pick set for the down and combine kernels; block (., u) works on distinct
-// expert u.  grid (I/16, min(E, T*k)), 128 * slices threads.
+// expert u.  grid (I/(16*RT), min(E, T*k)), 128 * RT * slices threads.
 template <int SPW, int NPL>
 __global__ __launch_bounds__(512) void ffn_gate_up_sel(const uint16_t *__restrict__ x, int H, int I, int k, int NT,
-                                                       SelectArgs sa, GroupOut o, uint16_t *__restrict__ hhi,
+                                                       int RT, SelectArgs sa, GroupOut o, uint16_t *__restrict__ hhi,
                                                        uint16_t *__restrict__ hlo) {
     extern __shared__ __align__(16) char smem[];
     __shared__ int sid[kFusedSelectPairs], sflag[kFusedSelectPairs], spl[kSmallRouteTokens], sinfo[4];
@@ -161,89 +179,125 @@ __global__ __launch_bounds__(512) void ffn_gate_up_sel(const uint16_t *__restric
     const int n = sinfo[0];
     const uint8_t *base = reinterpret_cast<const uint8_t *>(((uint64_t)(uint32_t)sinfo[3] << 32) | (uint32_t)sinfo[2]);
     if (n == 0 || base == nullptr) return;
-    gate_up_tile_blk<SPW>(x, H, I, k, NT, base, n, sinfo[1], [&](int c) { return spl[c]; }, smem, hhi, hlo);
+    gate_up_tile_blk<SPW>(x, H, I, k, NT, RT, base, n, sinfo[1], [&](int c) { return spl[c]; }, smem, hhi, hlo);
 }
 
-// grid (H/32, max distinct experts), 128 * slices threads; LDS: NT rows of h
-// hi and lo and the per-wave partial sums.
-template <int SPW>
-__global__ __launch_bounds__(512) void ffn_down_blk(int H, int I, int NT, GroupView gv,
+// grid (H/(16*RT), max distinct experts of the part), 64 * RT * slices
+// threads: RT row tiles of 16 rows x slices of K.  LDS: NT rows of h hi and
+// lo and the per-wave partial sums.
+template <int SPW, int RT, int PRE>
+__global__ __launch_bounds__(512) void ffn_down_blk(int H, int I, int NT, GroupView gv, int part,
                                                     const uint16_t *__restrict__ hhi,
                                                     const uint16_t *__restrict__ hlo, float *__restrict__ y) {
     extern __shared__ __align__(16) char smem[];
-    const int u = blockIdx.y;
-    if (u >= gv.nuniq[0]) return;
+    const int u = part_expert(gv, part);
+    if (u < 0) return;
     const uint8_t *base = reinterpret_cast<const uint8_t *>(gv.uptr[u]);
     const int n = gv.ucnt[u], q0 = gv.uoff[u];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
     const int nw = blockDim.x >> 6;
-    const int rt = wave & 1, slice = wave >> 1;   // 2 row tiles x slices
-    const int rb = blockIdx.x;
-    const int row0 = rb * 32;
+    const int rt = wave % RT, slice = wave / RT;
+    const int row0 = blockIdx.x * (16 * RT);
     const BlobLayout L = BlobLayout::make(H, I);
 
     if (base == nullptr) {   // unusable residency entry: its pairs contribute zero
-        for (int i = tid; i < n * 8; i += blockDim.x) {
-            const int p = gv.plist[q0 + i / 8];
-            reinterpret_cast<float4 *>(y + (size_t)p * H + row0)[i % 8] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int i = tid; i < n * 4 * RT; i += blockDim.x) {
+            const int p = gv.plist[q0 + i / (4 * RT)];
+            reinterpret_cast<float4 *>(y + (size_t)p * H + row0)[i % (4 * RT)] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
-    } else {
-        const size_t row = (size_t)row0 + rt * 16 + r;
-        const uint8_t *qp = base + L.w2_codes + row * (I / 2) + (size_t)slice * SPW * 64 + 16 * g;
-        const uint8_t *sp = base + L.w2_scales + row * (I / 32) + (size_t)slice * SPW * 4;
-        uint4 q[SPW];
-        uint32_t sc[SPW];
+        return;
+    }
+    const size_t row = (size_t)row0 + rt * 16 + r;
+    const uint8_t *qp = base + L.w2_codes + row * (I / 2) + (size_t)slice * SPW * 64 + 16 * g;
+    const uint8_t *sp = base + L.w2_scales + row * (I / 32) + (size_t)slice * SPW * 4;
+    // The vector memory counter retires in issue order, so a wait for a
+    // staged unit also waits for every load issued before it.  With PRE > 0
+    // the first PRE units per thread of the first pass's h rows (contiguous in
+    // grouped order) are requested ahead of the weights, scales before codes.
+    const int nch = I / 8, stride = nch + 1;   // 16-byte units per row; LDS rows padded
+    const int total0 = (n < NT ? n : NT) * nch;
+    const uint4 *sh0 = reinterpret_cast<const uint4 *>(hhi + (size_t)q0 * I);
+    const uint4 *sl0 = reinterpret_cast<const uint4 *>(hlo + (size_t)q0 * I);
+    constexpr int kPre = PRE > 0 ? PRE : 1;
+    u32x4 ph[kPre], pl[kPre];   // a plain vector type and unconditional loads: kept in registers
+    if constexpr (PRE > 0) {
 #pragma unroll
-        for (int i = 0; i < SPW; ++i) q[i] = gload16(qp + (size_t)i * 64);
+        for (int v = 0; v < PRE; ++v) {
+            const int i = tid + v * (int)blockDim.x;
+            const int ic = i < total0 ? i : total0 - 1;
+            ph[v] = reinterpret_cast<const u32x4 *>(sh0)[ic];
+            pl[v] = reinterpret_cast<const u32x4 *>(sl0)[ic];
+        }
+    }
+    uint32_t sc[SPW];
 #pragma unroll
-        for (int i = 0; i < SPW; ++i) sc[i] = gload<uint32_t>(sp + 4 * i);
+    for (int i = 0; i < SPW; ++i) sc[i] = gload<uint32_t>(sp + 4 * i);
+    uint4 q[SPW];
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) q[i] = gload16(qp + (size_t)i * 64);
+    __builtin_amdgcn_sched_barrier(0);
 
-        const int stride = I / 8 + 1;   // 16-byte units, padded
-        uint4 *hs = reinterpret_cast<uint4 *>(smem);
-        uint4 *ls = hs + (size_t)NT * stride;
-        f32x4 *red = reinterpret_cast<f32x4 *>(smem + (size_t)2 * NT * stride * 16);
-        for (int tb = 0; tb < n; tb += NT) {
-            const int nt = (n - tb) < NT ? (n - tb) : NT;
-            __syncthreads();
-            for (int c = 0; c < nt; ++c) {
-                const uint4 *sh = reinterpret_cast<const uint4 *>(hhi + (size_t)(q0 + tb + c) * I);
-                const uint4 *sl = reinterpret_cast<const uint4 *>(hlo + (size_t)(q0 + tb + c) * I);
-                for (int j = tid; j < I / 8; j += blockDim.x) {
-                    hs[c * stride + j] = sh[j];
-                    ls[c * stride + j] = sl[j];
-                }
-            }
-            __syncthreads();
-            const bool tv = r < nt;
-            const int lo = (tv ? r : 0) * stride + slice * SPW * 16 + 4 * g;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    uint4 *hs = reinterpret_cast<uint4 *>(smem);
+    uint4 *ls = hs + (size_t)NT * stride;
+    f32x4 *red = reinterpret_cast<f32x4 *>(smem + (size_t)2 * NT * stride * 16);
+    for (int tb = 0; tb < n; tb += NT) {
+        const int nt = (n - tb) < NT ? (n - tb) : NT;
+        __syncthreads();
+        int ifrom = 0;
+        if (PRE > 0 && tb == 0) {
 #pragma unroll
-            for (int i = 0; i < SPW; ++i) {
-                float s = e8m0_to_f32((sc[i] >> (8 * g)) & 0xffu);
-                asm volatile("" : "+v"(s));   // keep the converts at their step
-                const uint32_t w4[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const bf16x8 a = fp4x8_to_bf16x8(w4[m], s);
-                    acc = mfma16x16x32(a, as_bf16x8(hs[lo + i * 16 + m]), acc);
-                    acc = mfma16x16x32(a, as_bf16x8(ls[lo + i * 16 + m]), acc);
-                }
-                __builtin_amdgcn_sched_barrier(0);
+            for (int v = 0; v < kPre; ++v) {   // clamped units rewrite their own bytes
+                const int i = tid + v * (int)blockDim.x;
+                const int ic = i < total0 ? i : total0 - 1;
+                const int o = (ic / nch) * stride + ic % nch;
+                reinterpret_cast<u32x4 *>(hs)[o] = ph[v];
+                reinterpret_cast<u32x4 *>(ls)[o] = pl[v];
             }
-            red[wave * 64 + lane] = acc;
-            __syncthreads();
-            if (wave < 2) {   // wave rt adds its row tile's slices in a fixed order
-                f32x4 s = red[wave * 64 + lane];
-                for (int w2 = wave + 2; w2 < nw; w2 += 2) s += red[w2 * 64 + lane];
-                if (tv) {
-                    const int p = gv.plist[q0 + tb + r];
-                    *reinterpret_cast<float4 *>(y + (size_t)p * H + row0 + wave * 16 + 4 * g) =
-                        make_float4(s[0], s[1], s[2], s[3]);
-                }
+            ifrom = PRE * (int)blockDim.x;
+        }
+        {   // the rest of the pass's h rows, a batch of units at a time
+            const int total = nt * nch;
+            const uint4 *sh = reinterpret_cast<const uint4 *>(hhi + (size_t)(q0 + tb) * I);
+            const uint4 *sl = reinterpret_cast<const uint4 *>(hlo + (size_t)(q0 + tb) * I);
+            for (int i0 = ifrom + tid; i0 < total; i0 += 2 * blockDim.x) {
+                const int i1 = i0 + (int)blockDim.x < total ? i0 + (int)blockDim.x : i0;
+                const uint4 a = sh[i0], b = sl[i0], c = sh[i1], d = sl[i1];
+                const int o0 = (i0 / nch) * stride + i0 % nch, o1 = (i1 / nch) * stride + i1 % nch;
+                hs[o0] = a;
+                ls[o0] = b;
+                hs[o1] = c;
+                ls[o1] = d;
+            }
+        }
+        __syncthreads();
+        const bool tv = r < nt;
+        const int lo = (tv ? r : 0) * stride + slice * SPW * 16 + 4 * g;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            float s = e8m0_to_f32((sc[i] >> (8 * g)) & 0xffu);
+            asm volatile("" : "+v"(s));   // keep the converts at their step
+            const uint32_t w4[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const bf16x8 a = fp4x8_to_bf16x8(w4[m], s);
+                acc = mfma16x16x32(a, as_bf16x8(hs[lo + i * 16 + m]), acc);
+                acc = mfma16x16x32(a, as_bf16x8(ls[lo + i * 16 + m]), acc);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        red[wave * 64 + lane] = acc;
+        __syncthreads();
+        if (wave < RT) {   // wave rt adds its row tile's slices in a fixed order
+            f32x4 s = red[wave * 64 + lane];
+            for (int w2 = wave + RT; w2 < nw; w2 += RT) s += red[w2 * 64 + lane];
+            if (tv) {
+                const int p = gv.plist[q0 + tb + r];
+                *reinterpret_cast<float4 *>(y + (size_t)p * H + row0 + wave * 16 + 4 * g) =
+                    make_float4(s[0], s[1], s[2], s[3]);
             }
         }
     }
-
 }
 
 // ========================= general one-wave kernels =========================
@@ -450,83 +504,129 @@ int pick_spw(int steps, int max_slices) {
     return 0;
 }
 
+// Profiling name of a launch of one FFN part.
+const char *part_name(int part, const char *all, const char *hot, const char *cold) {
+    return part == kPartHot ? hot : part == kPartCold ? cold : all;
+}
+
 int stage_rows(int bytes_per_row) {
     const int nt = kStageBytes / bytes_per_row;
     return nt < 1 ? 1 : (nt > 16 ? 16 : nt);
 }
 
+// Gate/up block shape, a function of T and H only (an all-resident and a
+// mixed run of one batch then add in the same order): from kWideTokens
+// tokens two row tiles share a block, one staging of the token rows for twice
+// the weight rows.
+struct GateUpShape {
+    int rt, spw, slices;
+};
+GateUpShape gate_up_shape(int T, int H) {
+    const int steps = H / 128;
+    GateUpShape g;
+    g.rt = (T >= kWideTokens && pick_spw(steps, 2) != 0) ? 2 : 1;
+    g.spw = pick_spw(steps, 4 / g.rt);
+    g.slices = g.spw ? steps / g.spw : 0;
+    return g;
+}
+
 template <int SPW>
-void launch_gate_up_blk(const FfnArgs &a, const GroupView &gv, uint16_t *hhi, uint16_t *hlo, int umax,
-                        hipStream_t st) {
+void launch_gate_up_blk(const FfnArgs &a, const GroupView &gv, int part, int RT, uint16_t *hhi, uint16_t *hlo,
+                        int umax, hipStream_t st) {
     const int slices = a.H / 128 / SPW;
     const int row_bytes = (a.H / 8 + 1) * 16;
     const int NT = stage_rows(row_bytes);
-    const size_t lds = (size_t)NT * row_bytes + (size_t)2 * slices * 64 * 16;
-    MOE_LAUNCH("ffn_gate_up_blk", ffn_gate_up_blk<SPW>, dim3(a.I / 16, umax), dim3(128 * slices), lds, st, a.x,
-               a.H, a.I, a.k, NT, gv, hhi, hlo);
+    const size_t lds = (size_t)NT * row_bytes + (size_t)2 * RT * slices * 64 * 16;
+    MOE_LAUNCH(part_name(part, "ffn_gate_up_blk", "ffn_gate_up_blk_hot", "ffn_gate_up_blk_cold"),
+               ffn_gate_up_blk<SPW>, dim3(a.I / (16 * RT), umax), dim3(128 * RT * slices), lds, st, a.x, a.H, a.I,
+               a.k, NT, RT, gv, part, hhi, hlo);
 }
 
-template <int SPW>
-void launch_down_blk(const FfnArgs &a, const GroupView &gv, const uint16_t *hhi, const uint16_t *hlo, float *y,
-                     int umax, hipStream_t st) {
+template <int SPW, int RT, int PRE>
+void launch_down_blk(const FfnArgs &a, const GroupView &gv, int part, const uint16_t *hhi, const uint16_t *hlo,
+                     float *y, int umax, hipStream_t st) {
     const int slices = a.I / 128 / SPW;
     const int row_bytes = (a.I / 8 + 1) * 16;
     const int NT = stage_rows(2 * row_bytes);
-    const size_t lds = (size_t)2 * NT * row_bytes + (size_t)2 * slices * 64 * 16;
-    MOE_LAUNCH("ffn_down_blk", ffn_down_blk<SPW>, dim3(a.H / 32, umax), dim3(128 * slices), lds, st, a.H, a.I,
-               NT, gv, hhi, hlo, y);
+    const size_t lds = (size_t)2 * NT * row_bytes + (size_t)RT * slices * 64 * 16;
+    MOE_LAUNCH(part_name(part, "ffn_down_blk", "ffn_down_blk_hot", "ffn_down_blk_cold"),
+               (ffn_down_blk<SPW, RT, PRE>), dim3(a.H / (16 * RT), umax), dim3(64 * RT * slices), lds, st, a.H,
+               a.I, NT, gv, part, hhi, hlo, y);
 }
 
-void gate_up_blk(int spw, const FfnArgs &a, const GroupView &gv, uint16_t *hhi, uint16_t *hlo, int umax,
+void gate_up_blk(const FfnArgs &a, const GroupView &gv, int part, uint16_t *hhi, uint16_t *hlo, int umax,
                  hipStream_t st) {
-    switch (spw) {
-        case 1: launch_gate_up_blk<1>(a, gv, hhi, hlo, umax, st); break;
-        case 2: launch_gate_up_blk<2>(a, gv, hhi, hlo, umax, st); break;
-        case 4: launch_gate_up_blk<4>(a, gv, hhi, hlo, umax, st); break;
-        case 8: launch_gate_up_blk<8>(a, gv, hhi, hlo, umax, st); break;
-        default: launch_gate_up_blk<16>(a, gv, hhi, hlo, umax, st); break;
+    const GateUpShape g = gate_up_shape(a.T, a.H);
+    switch (g.spw) {
+        case 1: launch_gate_up_blk<1>(a, gv, part, g.rt, hhi, hlo, umax, st); break;
+        case 2: launch_gate_up_blk<2>(a, gv, part, g.rt, hhi, hlo, umax, st); break;
+        case 4: launch_gate_up_blk<4>(a, gv, part, g.rt, hhi, hlo, umax, st); break;
+        case 8: launch_gate_up_blk<8>(a, gv, part, g.rt, hhi, hlo, umax, st); break;
+        default: launch_gate_up_blk<16>(a, gv, part, g.rt, hhi, hlo, umax, st); break;
     }
 }
 
-void down_blk(int spw, const FfnArgs &a, const GroupView &gv, const uint16_t *hhi, const uint16_t *hlo, float *y,
-              int umax, hipStream_t st) {
+template <int RT, int PRE>
+void down_blk_rt(int spw, const FfnArgs &a, const GroupView &gv, int part, const uint16_t *hhi,
+                 const uint16_t *hlo, float *y, int umax, hipStream_t st) {
     switch (spw) {
-        case 1: launch_down_blk<1>(a, gv, hhi, hlo, y, umax, st); break;
-        case 2: launch_down_blk<2>(a, gv, hhi, hlo, y, umax, st); break;
-        case 4: launch_down_blk<4>(a, gv, hhi, hlo, y, umax, st); break;
-        case 8: launch_down_blk<8>(a, gv, hhi, hlo, y, umax, st); break;
-        default: launch_down_blk<16>(a, gv, hhi, hlo, y, umax, st); break;
+        case 1: launch_down_blk<1, RT, PRE>(a, gv, part, hhi, hlo, y, umax, st); break;
+        case 2: launch_down_blk<2, RT, PRE>(a, gv, part, hhi, hlo, y, umax, st); break;
+        case 4: launch_down_blk<4, RT, PRE>(a, gv, part, hhi, hlo, y, umax, st); break;
+        case 8: launch_down_blk<8, RT, PRE>(a, gv, part, hhi, hlo, y, umax, st); break;
+        default: launch_down_blk<16, RT, PRE>(a, gv, part, hhi, hlo, y, umax, st); break;
     }
+}
+
+// Down kernel shape.  More rows per block share one staging of the h rows,
+// which pays once experts see several tokens; with about one token per
+// expert, twice as many smaller blocks keep more loads in flight.
+void down_blk(const FfnArgs &a, const GroupView &gv, int part, const uint16_t *hhi, const uint16_t *hlo,
+              float *y, int umax, hipStream_t st) {
+    const int steps = a.I / 128;
+    const bool wide = a.T >= kWideTokens && a.H % 64 == 0 && pick_spw(steps, 2) != 0;
+    if (wide)
+        down_blk_rt<4, 1>(pick_spw(steps, 2), a, gv, part, hhi, hlo, y, umax, st);
+    else
+        down_blk_rt<2, 0>(pick_spw(steps, 4), a, gv, part, hhi, hlo, y, umax, st);
+}
+
+void launch_combine(const FfnArgs &a, const float *y, hipStream_t st) {
+    const int n4 = a.H / 4;
+    const int ty = a.T < 65535 ? a.T : 65535;
+    MOE_LAUNCH("ffn_combine", ffn_combine, dim3((n4 + 255) / 256, ty), dim3(256), 0, st, y, a.ids, a.w, a.T, a.H,
+               a.E, a.k, a.out_bf16, a.out);
 }
 
 }  // namespace
 
 template <int SPW, int NPL>
-void launch_gate_up_sel(const FfnArgs &a, const SelectArgs &sa, const GroupOut &o, uint16_t *hhi, uint16_t *hlo,
-                        int umax, hipStream_t st) {
+void launch_gate_up_sel(const FfnArgs &a, int RT, const SelectArgs &sa, const GroupOut &o, uint16_t *hhi,
+                        uint16_t *hlo, int umax, hipStream_t st) {
     const int slices = a.H / 128 / SPW;
     const int row_bytes = (a.H / 8 + 1) * 16;
     const int NT = stage_rows(row_bytes);
-    const size_t lds = (size_t)NT * row_bytes + (size_t)2 * slices * 64 * 16;
-    MOE_LAUNCH("ffn_gate_up_sel", (ffn_gate_up_sel<SPW, NPL>), dim3(a.I / 16, umax), dim3(128 * slices), lds, st,
-               a.x, a.H, a.I, a.k, NT, sa, o, hhi, hlo);
+    const size_t lds = (size_t)NT * row_bytes + (size_t)2 * RT * slices * 64 * 16;
+    MOE_LAUNCH("ffn_gate_up_sel", (ffn_gate_up_sel<SPW, NPL>), dim3(a.I / (16 * RT), umax),
+               dim3(128 * RT * slices), lds, st, a.x, a.H, a.I, a.k, NT, RT, sa, o, hhi, hlo);
 }
 
 template <int SPW>
-void gate_up_sel_npl(int npl, const FfnArgs &a, const SelectArgs &sa, const GroupOut &o, uint16_t *hhi,
+void gate_up_sel_npl(int npl, const FfnArgs &a, int RT, const SelectArgs &sa, const GroupOut &o, uint16_t *hhi,
                      uint16_t *hlo, int umax, hipStream_t st) {
     switch (npl) {
-        case 1: launch_gate_up_sel<SPW, 1>(a, sa, o, hhi, hlo, umax, st); break;
-        case 2: launch_gate_up_sel<SPW, 2>(a, sa, o, hhi, hlo, umax, st); break;
-        case 4: launch_gate_up_sel<SPW, 4>(a, sa, o, hhi, hlo, umax, st); break;
-        case 8: launch_gate_up_sel<SPW, 8>(a, sa, o, hhi, hlo, umax, st); break;
-        default: launch_gate_up_sel<SPW, 16>(a, sa, o, hhi, hlo, umax, st); break;
+        case 1: launch_gate_up_sel<SPW, 1>(a, RT, sa, o, hhi, hlo, umax, st); break;
+        case 2: launch_gate_up_sel<SPW, 2>(a, RT, sa, o, hhi, hlo, umax, st); break;
+        case 4: launch_gate_up_sel<SPW, 4>(a, RT, sa, o, hhi, hlo, umax, st); break;
+        case 8: launch_gate_up_sel<SPW, 8>(a, RT, sa, o, hhi, hlo, umax, st); break;
+        default: launch_gate_up_sel<SPW, 16>(a, RT, sa, o, hhi, hlo, umax, st); break;
     }
 }
 
 bool ffn_select_fusable(int T, int k, int H, int I) {
     if (!ffn_block_path(T, H, I)) return false;
-    const int P = T * k, threads = 128 * (H / 128 / pick_spw(H / 128, 4));
+    const GateUpShape g = gate_up_shape(T, H);
+    const int P = T * k, threads = 128 * g.rt * g.slices;
     return P <= kFusedSelectPairs && P <= threads;
 }
 
@@ -546,8 +646,8 @@ hipError_t launch_ffn(const FfnArgs &a, char *ws, const WsLayout &L, hipStream_t
         const hipError_t e = launch_ffn_gemm(a, gv, WsLayout::max_tiles(a.E, P), hhi, hlo, y, st);
         if (e != hipSuccess) return e;
     } else if (ffn_block_path(a.T, a.H, a.I)) {
-        gate_up_blk(pick_spw(a.H / 128, 4), a, gv, hhi, hlo, umax, st);
-        down_blk(pick_spw(a.I / 128, 4), a, gv, hhi, hlo, y, umax, st);
+        gate_up_blk(a, gv, kPartAll, hhi, hlo, umax, st);
+        down_blk(a, gv, kPartAll, hhi, hlo, y, umax, st);
     } else {
         const int sgu = a.H / 128;
         const dim3 ggu(a.I / 16, umax);
@@ -568,10 +668,7 @@ hipError_t launch_ffn(const FfnArgs &a, char *ws, const WsLayout &L, hipStream_t
             MOE_LAUNCH("ffn_down_wave", ffn_down_wave<1>, gd, dim3(64), 0, st, a.H, a.I, gv, hhi, hlo, y);
     }
 
-    const int n4 = a.H / 4;
-    const int ty = a.T < 65535 ? a.T : 65535;
-    MOE_LAUNCH("ffn_combine", ffn_combine, dim3((n4 + 255) / 256, ty), dim3(256), 0, st, y, a.ids, a.w, a.T, a.H,
-               a.E, a.k, a.out_bf16, a.out);
+    launch_combine(a, y, st);
     return hipGetLastError();
 }
 
@@ -586,18 +683,31 @@ hipError_t launch_ffn_select(const FfnArgs &a, const float *z, int renorm, int32
     uint16_t *hlo = hhi + P * (size_t)a.I;
     float *y = reinterpret_cast<float *>(ws + L.ybuf);
     const int npl = topk_npl(a.E);
-    switch (pick_spw(a.H / 128, 4)) {
-        case 1: gate_up_sel_npl<1>(npl, a, sa, o, hhi, hlo, umax, st); break;
-        case 2: gate_up_sel_npl<2>(npl, a, sa, o, hhi, hlo, umax, st); break;
-        case 4: gate_up_sel_npl<4>(npl, a, sa, o, hhi, hlo, umax, st); break;
-        case 8: gate_up_sel_npl<8>(npl, a, sa, o, hhi, hlo, umax, st); break;
-        default: gate_up_sel_npl<16>(npl, a, sa, o, hhi, hlo, umax, st); break;
+    const GateUpShape gs = gate_up_shape(a.T, a.H);
+    switch (gs.spw) {
+        case 1: gate_up_sel_npl<1>(npl, a, gs.rt, sa, o, hhi, hlo, umax, st); break;
+        case 2: gate_up_sel_npl<2>(npl, a, gs.rt, sa, o, hhi, hlo, umax, st); break;
+        case 4: gate_up_sel_npl<4>(npl, a, gs.rt, sa, o, hhi, hlo, umax, st); break;
+        case 8: gate_up_sel_npl<8>(npl, a, gs.rt, sa, o, hhi, hlo, umax, st); break;
+        default: gate_up_sel_npl<16>(npl, a, gs.rt, sa, o, hhi, hlo, umax, st); break;
     }
-    down_blk(pick_spw(a.I / 128, 4), a, gv, hhi, hlo, y, umax, st);
-    const int n4 = a.H / 4;
-    const int ty = a.T < 65535 ? a.T : 65535;
-    MOE_LAUNCH("ffn_combine", ffn_combine, dim3((n4 + 255) / 256, ty), dim3(256), 0, st, y, a.ids, a.w, a.T, a.H,
-               a.E, a.k, a.out_bf16, a.out);
+    down_blk(a, gv, kPartAll, hhi, hlo, y, umax, st);
+    launch_combine(a, y, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_ffn_part(const FfnArgs &a, int part, int umax_part, char *ws, const WsLayout &L,
+                           hipStream_t st) {
+    const GroupView gv = group_view(ws, L);
+    const size_t P = (size_t)a.T * a.k;
+    uint16_t *hhi = reinterpret_cast<uint16_t *>(ws + L.hbuf);
+    uint16_t *hlo = hhi + P * (size_t)a.I;
+    float *y = reinterpret_cast<float *>(ws + L.ybuf);
+    if (umax_part > 0) {
+        gate_up_blk(a, gv, part, hhi, hlo, umax_part, st);
+        down_blk(a, gv, part, hhi, hlo, y, umax_part, st);
+    }
+    if (part == kPartCold) launch_combine(a, y, st);
     return hipGetLastError();
 }
 

@@ -6,16 +6,23 @@
 //
 // Here the kernel reads the picked-cold list the grouping left in the
 // workspace (no host round trip) and streams each expert's bytes across the
-// host link with 128-bit device-initiated loads: every thread keeps four
-// loads in flight, a block covers 16 KB contiguous per iteration, and a wave
+// host link with 128-bit device-initiated loads: every thread keeps two loads
+// in flight, a block covers 8 KB contiguous per iteration, and a wave
 // instruction covers 1 KB contiguous.  Expert bytes are a multiple of 16.
+//
+// The grid is small on purpose: 32 blocks keep about 256 KB of host reads in
+// flight, which already holds the link at its measured rate (~56 GB/s).  A
+// grid eight times larger (2 MB in flight) copied no faster, and a kernel
+// running beside it (the hot experts' FFN during a layer's gather) started
+// 50-170 us late and ran up to five times slower; at 256 KB it starts within
+// about 20 us and runs 10-40% longer than alone.
 #include "kernels.hpp"
 
 namespace moe {
 
 constexpr int kGatherThreads = 256;
-constexpr int kGatherUnroll = 4;
-constexpr int kGatherBlocks = 1024;
+constexpr int kGatherUnroll = 2;
+constexpr int kGatherBlocks = 32;
 
 __global__ __launch_bounds__(kGatherThreads) void gather_cold(const uint8_t *__restrict__ host_cold,
                                                               uint8_t *__restrict__ scratch, size_t blob_bytes,

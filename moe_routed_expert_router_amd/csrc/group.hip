@@ -51,6 +51,7 @@ __global__ __launch_bounds__(1024) void group_scan(int nchunks, int E, const int
                                                    int32_t *__restrict__ nuniq, int32_t *__restrict__ uniq,
                                                    int32_t *__restrict__ ucnt, int32_t *__restrict__ uoff,
                                                    uint64_t *__restrict__ uptr, int32_t *__restrict__ cold,
+                                                   int32_t *__restrict__ ucold, int32_t *__restrict__ cu,
                                                    int32_t *__restrict__ status, int32_t *__restrict__ sync,
                                                    int32_t *__restrict__ tlist) {
     __shared__ int lds[40];
@@ -93,8 +94,12 @@ __global__ __launch_bounds__(1024) void group_scan(int nchunks, int E, const int
             ucnt[ui] = cnt;
             uoff[ui] = off;
             uptr[ui] = addr;
+            ucold[ui] = is_cold ? 1 : 0;
         }
-        if (is_cold) cold[ci] = e;
+        if (is_cold) {
+            cold[ci] = e;
+            cu[ci] = ui;
+        }
         for (int c = 0; c < nchunks; ++c) hist[(size_t)c * stride + e] += off;
     }
     if (e == 0) {
@@ -132,7 +137,8 @@ hipError_t launch_group(const GroupArgs &a, char *ws, const WsLayout &L, hipStre
                        reinterpret_cast<int32_t *>(ws + L.counts), reinterpret_cast<int32_t *>(ws + L.nuniq),
                        reinterpret_cast<int32_t *>(ws + L.uniq), reinterpret_cast<int32_t *>(ws + L.ucnt),
                        reinterpret_cast<int32_t *>(ws + L.uoff), reinterpret_cast<uint64_t *>(ws + L.uptr),
-                       reinterpret_cast<int32_t *>(ws + L.cold), reinterpret_cast<int32_t *>(ws + L.status),
+                       reinterpret_cast<int32_t *>(ws + L.cold), reinterpret_cast<int32_t *>(ws + L.ucold),
+                       reinterpret_cast<int32_t *>(ws + L.cu), reinterpret_cast<int32_t *>(ws + L.status),
                        reinterpret_cast<int32_t *>(ws + L.sync), reinterpret_cast<int32_t *>(ws + L.tlist));
     if (L.nchunks > 0) {
         MOE_LAUNCH("group_place", group_place, dim3(L.nchunks), dim3(kChunk), 0, st, a.ids, P, a.E, hist, rank,

@@ -71,6 +71,15 @@ struct FfnArgs {
 };
 hipError_t launch_ffn(const FfnArgs &a, char *ws, const WsLayout &L, hipStream_t st);
 
+// Decode FFN in two parts so that the hot experts' FFN can run while the cold
+// ones are still being gathered: kPartHot covers the distinct experts whose
+// blob is in HBM proper, kPartCold those read from a scratch slot (grid rows
+// = picked cold experts, at most umax_part), then the combine.  The two parts
+// together do exactly what launch_ffn does.  Needs ffn_block_path.
+constexpr int kPartAll = 0, kPartHot = 1, kPartCold = 2;
+hipError_t launch_ffn_part(const FfnArgs &a, int part, int umax_part, char *ws, const WsLayout &L,
+                           hipStream_t st);
+
 // Decode layer with no cold expert: the gate/up kernel recomputes the top-k
 // and the grouping in every block (block 0 publishes ids, w and the pick set),
 // then down and combine as in launch_ffn.  Needs ffn_select_fusable.

@@ -85,7 +85,11 @@ __device__ __forceinline__ void select_group_block(const SelectArgs &a, const Gr
             o.ucnt[ui] = cnt;
             o.uoff[ui] = lt;
             o.uptr[ui] = addr;
-            if (flag & 2) o.cold[ci] = e;
+            o.ucold[ui] = (flag >> 1) & 1;
+            if (flag & 2) {
+                o.cold[ci] = e;
+                o.cu[ci] = ui;
+            }
         }
         if (ui == want) {
             s.spl[eqb] = tid;

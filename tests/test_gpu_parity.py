@@ -175,6 +175,53 @@ def test_all_hot_equals_mixed_bitwise():
         mixed.close()
 
 
+def boost_cold(L, delta):
+    """Raise the router bias of L's cold experts by delta (oracle and GPU)."""
+    L.bias_np = L.bias_np.copy()
+    L.bias_np[L.cold] += np.float32(delta)
+    L.bias.copy_(torch.from_numpy(L.bias_np))
+
+
+@pytest.mark.parametrize("T,delta", [(32, 3.0), (5, 3.0), (32, 0.0)])
+def test_decode_cold_picks_overlapped(T, delta):
+    """Decode layer with many picked cold experts: the gather runs on the side
+    stream while the hot experts' FFN runs; ids, gathered bytes and outputs
+    must be as with every expert resident."""
+    wl = gen.workload("hotcold8")
+    L = Layer(wl, T=T)
+    hot = Layer(wl, T=T, all_hot=True)
+    try:
+        boost_cold(L, delta)
+        hot.bias_np = L.bias_np
+        hot.bias.copy_(L.bias)
+        L.scratch.fill_(0xEE)
+        a = L.forward()
+        b = hot.forward()
+        torch.cuda.synchronize()
+        ids = L.ids.cpu().numpy()
+        pc = ogather.picked_cold(ids, L.slot_np)
+        print(f"T={T} delta={delta}: picked cold {len(pc)}", flush=True)
+        if delta > 0:
+            assert len(pc) >= 3
+        assert torch.equal(L.ids, hot.ids)
+        assert torch.equal(a, b), "hot/cold placement changed the output bits"
+        host = L.host.np.reshape(L.n_cold, L.B)
+        scratch = L.scratch.cpu().numpy()
+        want_rows = {-int(L.slot_np[e]) - 1 for e in pc}
+        for cs in range(L.n_cold):
+            if cs in want_rows:
+                assert np.array_equal(scratch[cs], host[cs]), cs
+            else:
+                assert np.all(scratch[cs] == 0xEE), cs
+        rows = sorted({0, T // 2, T - 1})
+        ref = oracle_out(L, rows=rows)
+        assert np.array_equal(ids[rows], ref["ids"])
+        check_out(a.cpu().numpy()[rows], ref["out"])
+    finally:
+        L.close()
+        hot.close()
+
+
 @pytest.mark.parametrize("m", [1, 5, 129])
 def test_forced_cold_gather(m):
     """ids crafted to pick exactly m distinct cold experts (plus hot ones)."""
@@ -390,12 +437,15 @@ def test_gpu_error_paths():
     assert st == moe.MOE_ERR_MISALIGNED
 
 
-@pytest.mark.parametrize("name,T", [("tiny", 8), ("hotcold8", 8)])
-def test_graph_replay_matches_eager(name, T):
+@pytest.mark.parametrize("name,T,delta", [("tiny", 8, 0.0), ("hotcold8", 8, 0.0), ("hotcold8", 32, 3.0)])
+def test_graph_replay_matches_eager(name, T, delta):
     """The layer captured in a HIP graph gives the eager result on every
-    replay, with eager work and synchronisations between replays."""
+    replay, with eager work and synchronisations between replays (with cold
+    picks the capture holds the side-stream fork and join)."""
     L = Layer(gen.workload(name), T=T)
     try:
+        if delta:
+            boost_cold(L, delta)
         eager = L.forward().clone()
         eager_ids = L.ids.clone()
         torch.cuda.synchronize()
