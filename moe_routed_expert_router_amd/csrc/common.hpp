@@ -206,6 +206,12 @@ __device__ __forceinline__ uint4 gload16(const void *p) {
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// Buffer resource over `bytes` bytes at `base`: reads past the end (all
+// reads, for zero bytes) return 0 and touch no memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
     return __builtin_bit_cast(bf16x8, v);
 }

@@ -31,12 +31,15 @@
 //            hi and h lo (two MFMAs per K slice), y[pair][row] in fp32.
 // The block shapes depend only on T and the layer shape, never on where the
 // experts live, so all-resident and mixed runs still add in the same order.
+//   down + combine (T*k <= 8, one decode token): one block per 16-row tile
+//            runs every distinct expert, keeps the pairs' outputs in LDS and
+//            writes out[t] itself — no y round trip, no combine launch.
 // General kernels (any T): one wave per 16 rows.
-// Both end with the combine kernel: out[t] = sum_j w[t,j] * y[t*k+j] in j
-// order, no float atomics.  (Folding the combine into the down kernel through
-// a last-arriver counter needs an agent-scope release per block, which on
-// this GPU writes the XCD's L2 back each time and costs more than the launch
-// it saves.)
+// Otherwise the combine kernel follows: out[t] = sum_j w[t,j] * y[t*k+j] in j
+// order, no float atomics.  (Folding the combine into a down kernel whose
+// blocks each hold one expert needs a last-arriver counter and an
+// agent-scope release per block, which on this GPU writes the XCD's L2 back
+// each time and costs more than the launch it saves.)
 #include "kernels.hpp"
 #include "select.hpp"
 
@@ -297,6 +300,184 @@ __global__ __launch_bounds__(512) void ffn_down_blk(int H, int I, int NT, GroupV
                     make_float4(s[0], s[1], s[2], s[3]);
             }
         }
+    }
+}
+
+// ====================== down + combine for a few pairs =======================
+constexpr int kDcMaxPairs = 8;   // pairs (T*k) up to which down and combine run as one kernel
+constexpr int kDcHUnits = 4;     // h units (16 B) per thread and plane requested ahead of the weights
+constexpr size_t kMaxLdsBytes = 160 * 1024;   // LDS per workgroup on gfx950
+
+// Down projection and weighted combine for at most kDcMaxPairs pairs (one
+// decode token): one block per 16-row tile runs every distinct expert of the
+// batch, with all their weight loads in flight together, keeps the pairs'
+// outputs for its 16 rows in LDS and writes out[t][rows] itself, adding the
+// k picks of each token in j order.  This saves the combine launch and the
+// y round trip through HBM.  grid H/16; 64 * slices threads (K slices of
+// SPW steps).  LDS: the h hi and lo rows of every grouped pair, the
+// (expert, wave) partial sums and the grouped position of each pair.
+template <int SPW, int P>
+__global__ __launch_bounds__(512) void ffn_down_combine(int H, int I, int T, int k, int E, GroupView gv,
+                                                        const uint16_t *__restrict__ hhi,
+                                                        const uint16_t *__restrict__ hlo,
+                                                        const int32_t *__restrict__ ids, const float *__restrict__ w,
+                                                        int out_bf16, void *__restrict__ out) {
+    // P == T * k: one expert slot per pair (at most P distinct experts)
+    extern __shared__ __align__(16) char smem[];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
+    const int nw = blockDim.x >> 6, bd = blockDim.x;
+    const int row0 = blockIdx.x * 16;
+    const int nch = I / 8, stride = nch + 1, total = P * nch;
+    const BlobLayout L = BlobLayout::make(H, I);
+
+    // One round of reads of what the grouping published, none waiting for
+    // another (each round trip to data the previous kernel wrote costs about
+    // a microsecond): the distinct count, every slot's run start and blob
+    // address (slots past the count hold stale values and are masked below),
+    // the pairs' ids, weights and grouped order, and the h rows of all P
+    // grouped positions (rows past the valid pairs feed only output columns
+    // that are never read).  Per-pair values by unconditional clamped vector
+    // loads: a value loaded under a branch gets consumed inside it, which
+    // would wait for it at once.
+    const int U = gv.nuniq[0];
+    int uo_raw[P + 1];
+    uint64_t up_raw[P];
+#pragma unroll
+    for (int u = 0; u <= P; ++u) uo_raw[u] = gv.uoff[u < E ? u : E];
+#pragma unroll
+    for (int u = 0; u < P; ++u) up_raw[u] = gv.uptr[u < E ? u : E - 1];
+    const int tp = tid < P ? tid : P - 1;
+    const int m_id = ids[tp];
+    const float m_w = w[tp];
+    const int m_pl = gv.plist[tp];
+    const u32x4 *sh = reinterpret_cast<const u32x4 *>(hhi);
+    const u32x4 *sl = reinterpret_cast<const u32x4 *>(hlo);
+    u32x4 ph[kDcHUnits], pl[kDcHUnits];
+#pragma unroll
+    for (int v = 0; v < kDcHUnits; ++v) {
+        const int i = tid + v * bd;
+        const int ic = i < total ? i : total - 1;
+        ph[v] = sh[ic];
+        pl[v] = sl[ic];
+    }
+    int nq = 0;   // grouped (valid) pairs
+#pragma unroll
+    for (int u = 0; u <= P; ++u)
+        if (u == U) nq = uo_raw[u];
+    int uo[P + 1];
+    uint32_t okmask = 0;   // bit u: slot u is a distinct expert with a usable blob
+#pragma unroll
+    for (int u = 0; u <= P; ++u) uo[u] = u <= U ? uo_raw[u] : nq;
+#pragma unroll
+    for (int u = 0; u < P; ++u)
+        if (u < U && up_raw[u] != 0) okmask |= 1u << u;
+
+    // every slot loads unconditionally (a masked slot gets a zero-size
+    // resource whose reads return 0), so the compiler knows how many loads
+    // are in flight at every wait; scales before codes
+    const uint32_t row = (uint32_t)(row0 + r);
+    const uint32_t soff = (uint32_t)L.w2_scales + row * (uint32_t)(I / 32) + (uint32_t)(wave * SPW * 4);
+    const uint32_t qoff = (uint32_t)L.w2_codes + row * (uint32_t)(I / 2) + (uint32_t)(wave * SPW * 64 + 16 * g);
+    __amdgpu_buffer_rsrc_t rs[P];
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+        const bool ok = (okmask >> u) & 1u;
+        rs[u] = buffer_rsrc(ok ? reinterpret_cast<const void *>(up_raw[u]) : nullptr, ok ? (uint32_t)L.bytes : 0u);
+    }
+    uint32_t sc[P][SPW];
+    u32x4 q[P][SPW];
+#pragma unroll
+    for (int u = 0; u < P; ++u)
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) sc[u][i] = __builtin_amdgcn_raw_buffer_load_b32(rs[u], soff + 4 * i, 0, 0);
+#pragma unroll
+    for (int u = 0; u < P; ++u)
+#pragma unroll
+        for (int i = 0; i < SPW; ++i)
+            q[u][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs[u], qoff + 64 * i, 0, 0));
+    __builtin_amdgcn_sched_barrier(0);
+
+    uint4 *hs = reinterpret_cast<uint4 *>(smem);
+    uint4 *ls = hs + (size_t)P * stride;
+    f32x4 *red = reinterpret_cast<f32x4 *>(ls + (size_t)P * stride);   // [P][nw][64]
+    int *pu = reinterpret_cast<int *>(red + (size_t)P * nw * 64);      // [P] slot of pair p (-1: none)
+    int *pc = pu + P;                                                   // [P] its column in that slot's run
+    float *sw = reinterpret_cast<float *>(pc + P);                      // [P] weights (0: invalid id)
+    float *ys = sw + P;                                                 // [P][16] pair outputs of the rows
+#pragma unroll
+    for (int v = 0; v < kDcHUnits; ++v) {   // clamped units rewrite their own bytes
+        const int i = tid + v * bd;
+        const int ic = i < total ? i : total - 1;
+        const int o = (ic / nch) * stride + ic % nch;
+        reinterpret_cast<u32x4 *>(hs)[o] = ph[v];
+        reinterpret_cast<u32x4 *>(ls)[o] = pl[v];
+    }
+    for (int i = tid + kDcHUnits * bd; i < total; i += bd) {
+        const int o = (i / nch) * stride + i % nch;
+        hs[o] = reinterpret_cast<const uint4 *>(hhi)[i];
+        ls[o] = reinterpret_cast<const uint4 *>(hlo)[i];
+    }
+    if (tid < P) {
+        pu[tid] = -1;
+        sw[tid] = (m_id >= 0 && m_id < E) ? m_w : 0.f;
+    }
+    __syncthreads();
+    if (tid < nq) {   // grouped position tid holds pair m_pl of run u
+        int u = 0, start = uo[0];
+#pragma unroll
+        for (int v = 1; v < P; ++v)
+            if (uo[v] <= tid && v < U) {
+                u = v;
+                start = uo[v];
+            }
+        pu[m_pl] = u;
+        pc[m_pl] = tid - start;
+    }
+
+    // Every slot computes, branch-free (a masked slot multiplies zeros and
+    // its sums are never read): per-slot branches let the compiler merge the
+    // slots' bodies, and the merged body waits for all weights at once.
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+        const int n = uo[u + 1] - uo[u];
+        const int lo = (n > 0 ? uo[u] + (r < n ? r : 0) : 0) * stride + wave * SPW * 16 + 4 * g;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            float s = e8m0_to_f32((sc[u][i] >> (8 * g)) & 0xffu);
+            asm volatile("" : "+v"(s));
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const bf16x8 a = fp4x8_to_bf16x8(q[u][i][m], s);
+                acc = mfma16x16x32(a, as_bf16x8(hs[lo + i * 16 + m]), acc);
+                acc = mfma16x16x32(a, as_bf16x8(ls[lo + i * 16 + m]), acc);
+            }
+        }
+        red[(u * nw + wave) * 64 + lane] = acc;
+    }
+    __syncthreads();
+
+    // y of pair p for row rr: its slot's K-slice partials in slice order
+    // (an invalid id or an unusable residency entry gives 0)
+    for (int idx = tid; idx < P * 16; idx += bd) {
+        const int p = idx >> 4, rr = idx & 15, u = pu[p];
+        float y = 0.f;
+        if (u >= 0 && ((okmask >> u) & 1u)) {
+            const int ln = pc[p] + 16 * (rr >> 2);
+            for (int s2 = 0; s2 < nw; ++s2) y += red[(u * nw + s2) * 64 + ln][rr & 3];
+        }
+        ys[idx] = y;
+    }
+    __syncthreads();
+    // out[t][row0 + rr]: the k picks of token t added in j order
+    for (int idx = tid; idx < T * 16; idx += bd) {
+        const int t = idx >> 4, rr = idx & 15;
+        float acc = 0.f;
+        for (int j = 0; j < k; ++j) acc += sw[t * k + j] * ys[(t * k + j) * 16 + rr];
+        if (out_bf16)
+            static_cast<uint16_t *>(out)[(size_t)t * H + row0 + rr] = (uint16_t)f32_to_bf16_bits(acc);
+        else
+            static_cast<float *>(out)[(size_t)t * H + row0 + rr] = acc;
     }
 }
 
@@ -591,6 +772,52 @@ void down_blk(const FfnArgs &a, const GroupView &gv, int part, const uint16_t *h
         down_blk_rt<2, 0>(pick_spw(steps, 4), a, gv, part, hhi, hlo, y, umax, st);
 }
 
+// LDS bytes of ffn_down_combine, or 0 when the shape does not qualify.
+size_t down_combine_lds(int T, int k, int H, int I) {
+    const int P = T * k, spw = pick_spw(I / 128, 8);
+    if (P > kDcMaxPairs || H % 16 != 0 || spw == 0) return 0;
+    const int slices = I / 128 / spw;
+    const size_t lds = (size_t)2 * P * (I / 8 + 1) * 16 + (size_t)P * slices * 64 * 16 + (size_t)(3 + 16) * P * 4;
+    return lds <= kMaxLdsBytes ? lds : 0;
+}
+
+template <int SPW, int UMAX>
+void launch_down_combine_u(const FfnArgs &a, const GroupView &gv, const uint16_t *hhi, const uint16_t *hlo,
+                           size_t lds, hipStream_t st) {
+    const int slices = a.I / 128 / SPW;
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&ffn_down_combine<SPW, UMAX>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    MOE_LAUNCH("ffn_down_combine", (ffn_down_combine<SPW, UMAX>), dim3(a.H / 16), dim3(64 * slices), lds, st,
+               a.H, a.I, a.T, a.k, a.E, gv, hhi, hlo, a.ids, a.w, a.out_bf16, a.out);
+}
+
+template <int SPW>
+void launch_down_combine_spw(const FfnArgs &a, const GroupView &gv, const uint16_t *hhi, const uint16_t *hlo,
+                             size_t lds, hipStream_t st) {
+    switch (a.T * a.k) {   // the expert slots: exactly the pairs
+        case 1: launch_down_combine_u<SPW, 1>(a, gv, hhi, hlo, lds, st); break;
+        case 2: launch_down_combine_u<SPW, 2>(a, gv, hhi, hlo, lds, st); break;
+        case 3: launch_down_combine_u<SPW, 3>(a, gv, hhi, hlo, lds, st); break;
+        case 4: launch_down_combine_u<SPW, 4>(a, gv, hhi, hlo, lds, st); break;
+        case 5: launch_down_combine_u<SPW, 5>(a, gv, hhi, hlo, lds, st); break;
+        case 6: launch_down_combine_u<SPW, 6>(a, gv, hhi, hlo, lds, st); break;
+        case 7: launch_down_combine_u<SPW, 7>(a, gv, hhi, hlo, lds, st); break;
+        default: launch_down_combine_u<SPW, 8>(a, gv, hhi, hlo, lds, st); break;
+    }
+}
+
+void launch_down_combine(const FfnArgs &a, const GroupView &gv, const uint16_t *hhi, const uint16_t *hlo,
+                         hipStream_t st) {
+    const size_t lds = down_combine_lds(a.T, a.k, a.H, a.I);
+    switch (pick_spw(a.I / 128, 8)) {
+        case 1: launch_down_combine_spw<1>(a, gv, hhi, hlo, lds, st); break;
+        case 2: launch_down_combine_spw<2>(a, gv, hhi, hlo, lds, st); break;
+        case 4: launch_down_combine_spw<4>(a, gv, hhi, hlo, lds, st); break;
+        case 8: launch_down_combine_spw<8>(a, gv, hhi, hlo, lds, st); break;
+        default: launch_down_combine_spw<16>(a, gv, hhi, hlo, lds, st); break;
+    }
+}
+
 void launch_combine(const FfnArgs &a, const float *y, hipStream_t st) {
     const int n4 = a.H / 4;
     const int ty = a.T < 65535 ? a.T : 65535;
@@ -647,6 +874,10 @@ hipError_t launch_ffn(const FfnArgs &a, char *ws, const WsLayout &L, hipStream_t
         if (e != hipSuccess) return e;
     } else if (ffn_block_path(a.T, a.H, a.I)) {
         gate_up_blk(a, gv, kPartAll, hhi, hlo, umax, st);
+        if (down_combine_lds(a.T, a.k, a.H, a.I)) {
+            launch_down_combine(a, gv, hhi, hlo, st);
+            return hipGetLastError();
+        }
         down_blk(a, gv, kPartAll, hhi, hlo, y, umax, st);
     } else {
         const int sgu = a.H / 128;
@@ -691,8 +922,12 @@ hipError_t launch_ffn_select(const FfnArgs &a, const float *z, int renorm, int32
         case 8: gate_up_sel_npl<8>(npl, a, gs.rt, sa, o, hhi, hlo, umax, st); break;
         default: gate_up_sel_npl<16>(npl, a, gs.rt, sa, o, hhi, hlo, umax, st); break;
     }
-    down_blk(a, gv, kPartAll, hhi, hlo, y, umax, st);
-    launch_combine(a, y, st);
+    if (down_combine_lds(a.T, a.k, a.H, a.I)) {
+        launch_down_combine(a, gv, hhi, hlo, st);
+    } else {
+        down_blk(a, gv, kPartAll, hhi, hlo, y, umax, st);
+        launch_combine(a, y, st);
+    }
     return hipGetLastError();
 }
 
@@ -703,11 +938,20 @@ hipError_t launch_ffn_part(const FfnArgs &a, int part, int umax_part, char *ws, 
     uint16_t *hhi = reinterpret_cast<uint16_t *>(ws + L.hbuf);
     uint16_t *hlo = hhi + P * (size_t)a.I;
     float *y = reinterpret_cast<float *>(ws + L.ybuf);
+    // with few pairs the down projection runs fused with the combine over
+    // every expert after the cold part's gate/up (the same kernel as in the
+    // all-resident sequence, so the results stay bit-identical)
+    const bool fused = down_combine_lds(a.T, a.k, a.H, a.I) != 0;
     if (umax_part > 0) {
         gate_up_blk(a, gv, part, hhi, hlo, umax_part, st);
-        down_blk(a, gv, part, hhi, hlo, y, umax_part, st);
+        if (!fused) down_blk(a, gv, part, hhi, hlo, y, umax_part, st);
     }
-    if (part == kPartCold) launch_combine(a, y, st);
+    if (part == kPartCold) {
+        if (fused)
+            launch_down_combine(a, gv, hhi, hlo, st);
+        else
+            launch_combine(a, y, st);
+    }
     return hipGetLastError();
 }
 

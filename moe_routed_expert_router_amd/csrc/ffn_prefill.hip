@@ -82,11 +82,6 @@ __device__ __forceinline__ T lds_ld(const uint8_t *p) {
 // the same idea with 64-byte (gate/up) or 32-byte (down) rows.
 constexpr int kXBytes = kPT * 256;
 
-// Buffer resource over `bytes` bytes at `base` (reads past the end return 0).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
-
 // N (16 or 4) bytes per lane from rsrc + voff into LDS at wave base +
 // N * lane.  Buffer (not flat) loads, so pending fills do not force the
 // compiler to drain every LDS read before its use.  (Sub-dword sizes would
