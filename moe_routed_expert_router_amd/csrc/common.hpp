@@ -212,6 +212,37 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, 
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// N (16 or 4) bytes per lane from rsrc + voff into LDS at wave base +
+// N * lane.  Buffer (not flat) loads, so pending fills do not force the
+// compiler to drain every LDS read before its use.  (Sub-dword sizes would
+// still place lanes 4 bytes apart, so they are not used.)
+template <int N>
+__device__ __forceinline__ void lds_fill(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint8_t *lds_wave_base) {
+    static_assert(N == 16 || N == 4, "fill size");
+    auto *d = (void __attribute__((address_space(3))) *)lds_wave_base;
+    if constexpr (N == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, voff, 0, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 4, voff, 0, 0, 0);
+}
+
+// Wait for all of this wave's outstanding global loads (LDS fills included).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+
+// Workgroup barrier for LDS fills issued before N (<= 63) later global loads
+// of this wave: wait until at most N of its loads are outstanding (the
+// counter retires in issue order, so the fills are done) and its LDS
+// operations are done, then meet the other waves.  Unlike __syncthreads
+// this does not wait for the N later loads.
+template <int N>
+__device__ __forceinline__ void fill_barrier() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0070 | (N & 15) | ((N >> 4) << 14));   // vmcnt(N) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
     return __builtin_bit_cast(bf16x8, v);
 }

@@ -66,17 +66,44 @@ __device__ __forceinline__ void split_store_h(const f32x4 &g, const f32x4 &u, ui
 }  // namespace
 
 // ============================ decode block kernels ==========================
-constexpr int kStageBytes = 49152;   // LDS budget for staged tokens / h rows
+constexpr int kStageBytes = 49152;   // LDS budget for staged tokens / h rows (3 blocks per CU)
+constexpr int kStageBytesWide = 67584;   // two-tile gate/up blocks (2 per CU by registers): 8 rows of H = 4096
 constexpr int kWideTokens = 8;       // tokens from which blocks take more weight rows
+constexpr int kDmaRows = 8;          // first-pass token rows staged by LDS DMA
 
-// Distinct expert of this block for an FFN part (FfnPart), or -1 when the
-// block has none: every distinct expert belongs to exactly one of the hot and
-// cold parts, so the hot and cold launches together equal one kPartAll launch.
-__device__ __forceinline__ int part_expert(const GroupView &gv, int part) {
-    const int b = blockIdx.y;
-    if (part == kPartCold) return b < gv.nuniq[1] ? gv.cu[b] : -1;
-    if (b >= gv.nuniq[0]) return -1;
-    return (part == kPartHot && gv.ucold[b]) ? -1 : b;
+// The distinct expert of this block for an FFN part (kPartAll / Hot / Cold)
+// and its blob address, pair count and run start; false when the block has
+// none.  Every distinct expert belongs to exactly one of the hot and cold
+// parts, so the hot and cold launches together equal one kPartAll launch.
+// All reads are issued in one round (each round trip to what the grouping
+// just wrote costs about a microsecond); only the cold part needs a second,
+// through its list of picked cold experts.
+struct PartExpert {
+    const uint8_t *base;
+    int n, q0;
+};
+__device__ __forceinline__ bool part_expert(const GroupView &gv, int part, PartExpert &pe) {
+    const int b = blockIdx.y;   // < grid rows <= min(E, T*k): every read below is in bounds
+    const int nu0 = gv.nuniq[0], nu1 = gv.nuniq[1], cold_b = gv.ucold[b];
+    uint64_t ptr = gv.uptr[b];
+    int n = gv.ucnt[b], q0 = gv.uoff[b];
+    // use every value at one point, so the compiler cannot sink a load into
+    // the branch that needs it and chain the round trips
+    asm volatile("" ::"s"(nu0), "s"(nu1), "s"(cold_b), "s"(n), "s"(q0), "s"((uint32_t)ptr),
+                 "s"((uint32_t)(ptr >> 32)));
+    if (part == kPartCold) {
+        if (b >= nu1) return false;
+        const int u = gv.cu[b];
+        ptr = gv.uptr[u];
+        n = gv.ucnt[u];
+        q0 = gv.uoff[u];
+    } else if (b >= nu0 || (part == kPartHot && cold_b)) {
+        return false;
+    }
+    pe.base = reinterpret_cast<const uint8_t *>(ptr);
+    pe.n = n;
+    pe.q0 = q0;
+    return true;
 }
 
 // RT 16-row tiles of one expert in the decode gate/up: the expert's blob at
@@ -97,26 +124,59 @@ __device__ __forceinline__ void gate_up_tile_blk(const uint16_t *__restrict__ x,
     const uint8_t *qp = base + L.w13_codes + row * (H / 2) + (size_t)slice * SPW * 64 + 16 * g;
     const uint8_t *sp = base + L.w13_scales + row * (H / 32) + (size_t)slice * SPW * 4;
 
-    // every weight load of this wave's slice, in flight together
+    // LDS rows in 16-byte units, padded by one unit: conflict-free token reads
+    const int nch = H / 8, stride = nch + 1;
+    uint4 *xs = reinterpret_cast<uint4 *>(smem);
+    f32x4 *red = reinterpret_cast<f32x4 *>(smem + (size_t)NT * stride * 16);
+
+    // The first pass's token rows go to LDS by DMA ahead of the weight loads
+    // (one 1 KB fill per wave and row, no registers held).  The vector memory
+    // counter retires in issue order, so waiting for the fills leaves the
+    // weights in flight, and the MFMAs then wait for the codes step by step.
+    const bool dma = nch % 64 == 0 && nch / 64 <= nw;
+    const int ndma = (n < NT ? n : NT) < kDmaRows ? (n < NT ? n : NT) : kDmaRows;
+    if (dma && wave < nch / 64) {
+        const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(x, 0xFFFFFFF0u);
+        // the rows' pair ids in one round: lane c reads row c's, then each
+        // row's token is broadcast from its lane
+        const int my_tok = pair_of(lane < ndma ? lane : ndma - 1) / k;
+#pragma unroll
+        for (int c = 0; c < kDmaRows; ++c)
+            if (c < ndma) {
+                const int tok = __builtin_amdgcn_readlane(my_tok, c);
+                lds_fill<16>(xrs, (uint32_t)((size_t)tok * H + (wave * 64 + lane) * 8) * 2u,
+                             reinterpret_cast<uint8_t *>(xs + c * stride) + wave * 1024);
+            }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // every weight load of this wave's slice, in flight together: codes,
+    // then scales (the fills' wait counts both as still outstanding)
     uint4 q[SPW];
     uint32_t sc[SPW];
 #pragma unroll
     for (int i = 0; i < SPW; ++i) q[i] = gload16(qp + (size_t)i * 64);
 #pragma unroll
     for (int i = 0; i < SPW; ++i) sc[i] = gload<uint32_t>(sp + 4 * i);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // LDS rows in 16-byte units, padded by one unit: conflict-free token reads
-    const int stride = H / 8 + 1;
-    uint4 *xs = reinterpret_cast<uint4 *>(smem);
-    f32x4 *red = reinterpret_cast<f32x4 *>(smem + (size_t)NT * stride * 16);
     for (int tb = 0; tb < n; tb += NT) {
         const int nt = (n - tb) < NT ? (n - tb) : NT;
-        __syncthreads();
-        for (int c = 0; c < nt; ++c) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)(pair_of(tb + c) / k) * H);
-            for (int j = tid; j < H / 8; j += blockDim.x) xs[c * stride + j] = src[j];
+        if (tb == 0 && dma) {
+            for (int c = ndma; c < nt; ++c) {   // rows past kDmaRows (small H only): copied
+                const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)(pair_of(c) / k) * H);
+                for (int j = tid; j < nch; j += blockDim.x) xs[c * stride + j] = src[j];
+            }
+            // the weight loads retire after the fills; the scales may have
+            // been merged into as few as SPW/4 loads
+            fill_barrier<SPW + (SPW + 3) / 4>();
+        } else {
+            __syncthreads();
+            for (int c = 0; c < nt; ++c) {
+                const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)(pair_of(tb + c) / k) * H);
+                for (int j = tid; j < nch; j += blockDim.x) xs[c * stride + j] = src[j];
+            }
+            __syncthreads();
         }
-        __syncthreads();
         // MFMA output columns are independent, so a lane whose token column is
         // empty reads row 0 and its column is never stored: no masked reads
         const bool tv = r < nt;   // this lane's token column
@@ -124,7 +184,11 @@ __device__ __forceinline__ void gate_up_tile_blk(const uint16_t *__restrict__ x,
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
-            float s = e8m0_to_f32((sc[i] >> (8 * g)) & 0xffu);
+            // the scale is read here, at its step (its load was issued last;
+            // a convert hoisted above the fill barrier would wait for it)
+            uint32_t scv = sc[i];
+            asm volatile("" : "+v"(scv));
+            float s = e8m0_to_f32((scv >> (8 * g)) & 0xffu);
             // converted weights are loop-invariant across token passes; keep
             // the converts at their step instead of holding 4x the registers
             asm volatile("" : "+v"(s));
@@ -158,12 +222,10 @@ __global__ __launch_bounds__(512) void ffn_gate_up_blk(const uint16_t *__restric
                                                        int NT, int RT, GroupView gv, int part, uint16_t *__restrict__ hhi,
                                                        uint16_t *__restrict__ hlo) {
     extern __shared__ __align__(16) char smem[];
-    const int u = part_expert(gv, part);
-    if (u < 0) return;
-    const uint8_t *base = reinterpret_cast<const uint8_t *>(gv.uptr[u]);
-    if (base == nullptr) return;
-    const int q0 = gv.uoff[u];
-    gate_up_tile_blk<SPW>(x, H, I, k, NT, RT, base, gv.ucnt[u], q0, [&](int c) { return gv.plist[q0 + c]; }, smem,
+    PartExpert pe;
+    if (!part_expert(gv, part, pe) || pe.base == nullptr) return;
+    const int q0 = pe.q0;
+    gate_up_tile_blk<SPW>(x, H, I, k, NT, RT, pe.base, pe.n, q0, [&](int c) { return gv.plist[q0 + c]; }, smem,
                           hhi, hlo);
 }
 
@@ -188,15 +250,15 @@ __global__ __launch_bounds__(512) void ffn_gate_up_sel(const uint16_t *__restric
 // grid (H/(16*RT), max distinct experts of the part), 64 * RT * slices
 // threads: RT row tiles of 16 rows x slices of K.  LDS: NT rows of h hi and
 // lo and the per-wave partial sums.
-template <int SPW, int RT, int PRE>
+template <int SPW, int RT>
 __global__ __launch_bounds__(512) void ffn_down_blk(int H, int I, int NT, GroupView gv, int part,
                                                     const uint16_t *__restrict__ hhi,
                                                     const uint16_t *__restrict__ hlo, float *__restrict__ y) {
     extern __shared__ __align__(16) char smem[];
-    const int u = part_expert(gv, part);
-    if (u < 0) return;
-    const uint8_t *base = reinterpret_cast<const uint8_t *>(gv.uptr[u]);
-    const int n = gv.ucnt[u], q0 = gv.uoff[u];
+    PartExpert pe;
+    if (!part_expert(gv, part, pe)) return;
+    const uint8_t *base = pe.base;
+    const int n = pe.n, q0 = pe.q0;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
     const int nw = blockDim.x >> 6;
     const int rt = wave % RT, slice = wave / RT;
@@ -213,56 +275,47 @@ __global__ __launch_bounds__(512) void ffn_down_blk(int H, int I, int NT, GroupV
     const size_t row = (size_t)row0 + rt * 16 + r;
     const uint8_t *qp = base + L.w2_codes + row * (I / 2) + (size_t)slice * SPW * 64 + 16 * g;
     const uint8_t *sp = base + L.w2_scales + row * (I / 32) + (size_t)slice * SPW * 4;
-    // The vector memory counter retires in issue order, so a wait for a
-    // staged unit also waits for every load issued before it.  With PRE > 0
-    // the first PRE units per thread of the first pass's h rows (contiguous in
-    // grouped order) are requested ahead of the weights, scales before codes.
     const int nch = I / 8, stride = nch + 1;   // 16-byte units per row; LDS rows padded
-    const int total0 = (n < NT ? n : NT) * nch;
-    const uint4 *sh0 = reinterpret_cast<const uint4 *>(hhi + (size_t)q0 * I);
-    const uint4 *sl0 = reinterpret_cast<const uint4 *>(hlo + (size_t)q0 * I);
-    constexpr int kPre = PRE > 0 ? PRE : 1;
-    u32x4 ph[kPre], pl[kPre];   // a plain vector type and unconditional loads: kept in registers
-    if constexpr (PRE > 0) {
-#pragma unroll
-        for (int v = 0; v < PRE; ++v) {
-            const int i = tid + v * (int)blockDim.x;
-            const int ic = i < total0 ? i : total0 - 1;
-            ph[v] = reinterpret_cast<const u32x4 *>(sh0)[ic];
-            pl[v] = reinterpret_cast<const u32x4 *>(sl0)[ic];
-        }
-    }
-    uint32_t sc[SPW];
-#pragma unroll
-    for (int i = 0; i < SPW; ++i) sc[i] = gload<uint32_t>(sp + 4 * i);
-    uint4 q[SPW];
-#pragma unroll
-    for (int i = 0; i < SPW; ++i) q[i] = gload16(qp + (size_t)i * 64);
-    __builtin_amdgcn_sched_barrier(0);
-
     uint4 *hs = reinterpret_cast<uint4 *>(smem);
     uint4 *ls = hs + (size_t)NT * stride;
     f32x4 *red = reinterpret_cast<f32x4 *>(smem + (size_t)2 * NT * stride * 16);
+
+    // The first pass's h rows (contiguous in grouped order, hi and lo
+    // planes) go to LDS by DMA ahead of the weight loads, as in the gate/up
+    // tile: one 1 KB fill per wave and chunk, no registers held, and the
+    // fills' wait leaves the weights in flight.
+    const int ncp = nch / 64;   // 1 KB chunks per row and plane
+    const bool dma = nch % 64 == 0;
+    const int ndma = n < NT ? n : NT;
+    if (dma) {
+        const __amdgpu_buffer_rsrc_t hrs = buffer_rsrc(hhi, 0xFFFFFFF0u);
+        const uint32_t lo_off = (uint32_t)((hlo - hhi) * 2);   // the lo plane, in bytes past hhi
+        for (int ch = wave; ch < 2 * ncp; ch += nw) {
+            const int pl = ch / ncp, cc = ch % ncp;
+            for (int c = 0; c < ndma; ++c)
+                lds_fill<16>(hrs, (pl ? lo_off : 0u) + (uint32_t)(((size_t)(q0 + c) * I + (cc * 64 + lane) * 8) * 2),
+                             reinterpret_cast<uint8_t *>((pl ? ls : hs) + c * stride) + cc * 1024);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 q[SPW];   // codes, then scales (the fills' wait counts both as outstanding)
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) q[i] = gload16(qp + (size_t)i * 64);
+    uint32_t sc[SPW];
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) sc[i] = gload<uint32_t>(sp + 4 * i);
+    __builtin_amdgcn_sched_barrier(0);
+
     for (int tb = 0; tb < n; tb += NT) {
         const int nt = (n - tb) < NT ? (n - tb) : NT;
-        __syncthreads();
-        int ifrom = 0;
-        if (PRE > 0 && tb == 0) {
-#pragma unroll
-            for (int v = 0; v < kPre; ++v) {   // clamped units rewrite their own bytes
-                const int i = tid + v * (int)blockDim.x;
-                const int ic = i < total0 ? i : total0 - 1;
-                const int o = (ic / nch) * stride + ic % nch;
-                reinterpret_cast<u32x4 *>(hs)[o] = ph[v];
-                reinterpret_cast<u32x4 *>(ls)[o] = pl[v];
-            }
-            ifrom = PRE * (int)blockDim.x;
-        }
-        {   // the rest of the pass's h rows, a batch of units at a time
+        if (tb == 0 && dma) {
+            fill_barrier<SPW + (SPW + 3) / 4>();
+        } else {   // copied (later passes of experts with more than NT tokens)
+            __syncthreads();
             const int total = nt * nch;
             const uint4 *sh = reinterpret_cast<const uint4 *>(hhi + (size_t)(q0 + tb) * I);
             const uint4 *sl = reinterpret_cast<const uint4 *>(hlo + (size_t)(q0 + tb) * I);
-            for (int i0 = ifrom + tid; i0 < total; i0 += 2 * blockDim.x) {
+            for (int i0 = tid; i0 < total; i0 += 2 * blockDim.x) {
                 const int i1 = i0 + (int)blockDim.x < total ? i0 + (int)blockDim.x : i0;
                 const uint4 a = sh[i0], b = sl[i0], c = sh[i1], d = sl[i1];
                 const int o0 = (i0 / nch) * stride + i0 % nch, o1 = (i1 / nch) * stride + i1 % nch;
@@ -271,14 +324,16 @@ __global__ __launch_bounds__(512) void ffn_down_blk(int H, int I, int NT, GroupV
                 hs[o1] = c;
                 ls[o1] = d;
             }
+            __syncthreads();
         }
-        __syncthreads();
         const bool tv = r < nt;
         const int lo = (tv ? r : 0) * stride + slice * SPW * 16 + 4 * g;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
-            float s = e8m0_to_f32((sc[i] >> (8 * g)) & 0xffu);
+            uint32_t scv = sc[i];   // read at its step (the scales were issued last)
+            asm volatile("" : "+v"(scv));
+            float s = e8m0_to_f32((scv >> (8 * g)) & 0xffu);
             asm volatile("" : "+v"(s));   // keep the converts at their step
             const uint32_t w4[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
 #pragma unroll
@@ -690,8 +745,8 @@ const char *part_name(int part, const char *all, const char *hot, const char *co
     return part == kPartHot ? hot : part == kPartCold ? cold : all;
 }
 
-int stage_rows(int bytes_per_row) {
-    const int nt = kStageBytes / bytes_per_row;
+int stage_rows(int bytes_per_row, int budget = kStageBytes) {
+    const int nt = budget / bytes_per_row;
     return nt < 1 ? 1 : (nt > 16 ? 16 : nt);
 }
 
@@ -716,22 +771,22 @@ void launch_gate_up_blk(const FfnArgs &a, const GroupView &gv, int part, int RT,
                         int umax, hipStream_t st) {
     const int slices = a.H / 128 / SPW;
     const int row_bytes = (a.H / 8 + 1) * 16;
-    const int NT = stage_rows(row_bytes);
+    const int NT = stage_rows(row_bytes, RT == 2 ? kStageBytesWide : kStageBytes);
     const size_t lds = (size_t)NT * row_bytes + (size_t)2 * RT * slices * 64 * 16;
     MOE_LAUNCH(part_name(part, "ffn_gate_up_blk", "ffn_gate_up_blk_hot", "ffn_gate_up_blk_cold"),
                ffn_gate_up_blk<SPW>, dim3(a.I / (16 * RT), umax), dim3(128 * RT * slices), lds, st, a.x, a.H, a.I,
                a.k, NT, RT, gv, part, hhi, hlo);
 }
 
-template <int SPW, int RT, int PRE>
+template <int SPW, int RT>
 void launch_down_blk(const FfnArgs &a, const GroupView &gv, int part, const uint16_t *hhi, const uint16_t *hlo,
                      float *y, int umax, hipStream_t st) {
     const int slices = a.I / 128 / SPW;
     const int row_bytes = (a.I / 8 + 1) * 16;
-    const int NT = stage_rows(2 * row_bytes);
+    const int NT = stage_rows(2 * row_bytes);   // measured: more rows (fewer blocks per CU) is slower here
     const size_t lds = (size_t)2 * NT * row_bytes + (size_t)RT * slices * 64 * 16;
     MOE_LAUNCH(part_name(part, "ffn_down_blk", "ffn_down_blk_hot", "ffn_down_blk_cold"),
-               (ffn_down_blk<SPW, RT, PRE>), dim3(a.H / (16 * RT), umax), dim3(64 * RT * slices), lds, st, a.H,
+               (ffn_down_blk<SPW, RT>), dim3(a.H / (16 * RT), umax), dim3(64 * RT * slices), lds, st, a.H,
                a.I, NT, gv, part, hhi, hlo, y);
 }
 
@@ -747,15 +802,15 @@ void gate_up_blk(const FfnArgs &a, const GroupView &gv, int part, uint16_t *hhi,
     }
 }
 
-template <int RT, int PRE>
+template <int RT>
 void down_blk_rt(int spw, const FfnArgs &a, const GroupView &gv, int part, const uint16_t *hhi,
                  const uint16_t *hlo, float *y, int umax, hipStream_t st) {
     switch (spw) {
-        case 1: launch_down_blk<1, RT, PRE>(a, gv, part, hhi, hlo, y, umax, st); break;
-        case 2: launch_down_blk<2, RT, PRE>(a, gv, part, hhi, hlo, y, umax, st); break;
-        case 4: launch_down_blk<4, RT, PRE>(a, gv, part, hhi, hlo, y, umax, st); break;
-        case 8: launch_down_blk<8, RT, PRE>(a, gv, part, hhi, hlo, y, umax, st); break;
-        default: launch_down_blk<16, RT, PRE>(a, gv, part, hhi, hlo, y, umax, st); break;
+        case 1: launch_down_blk<1, RT>(a, gv, part, hhi, hlo, y, umax, st); break;
+        case 2: launch_down_blk<2, RT>(a, gv, part, hhi, hlo, y, umax, st); break;
+        case 4: launch_down_blk<4, RT>(a, gv, part, hhi, hlo, y, umax, st); break;
+        case 8: launch_down_blk<8, RT>(a, gv, part, hhi, hlo, y, umax, st); break;
+        default: launch_down_blk<16, RT>(a, gv, part, hhi, hlo, y, umax, st); break;
     }
 }
 
@@ -767,9 +822,9 @@ void down_blk(const FfnArgs &a, const GroupView &gv, int part, const uint16_t *h
     const int steps = a.I / 128;
     const bool wide = a.T >= kWideTokens && a.H % 64 == 0 && pick_spw(steps, 2) != 0;
     if (wide)
-        down_blk_rt<4, 1>(pick_spw(steps, 2), a, gv, part, hhi, hlo, y, umax, st);
+        down_blk_rt<4>(pick_spw(steps, 2), a, gv, part, hhi, hlo, y, umax, st);
     else
-        down_blk_rt<2, 0>(pick_spw(steps, 4), a, gv, part, hhi, hlo, y, umax, st);
+        down_blk_rt<2>(pick_spw(steps, 4), a, gv, part, hhi, hlo, y, umax, st);
 }
 
 // LDS bytes of ffn_down_combine, or 0 when the shape does not qualify.
@@ -832,7 +887,7 @@ void launch_gate_up_sel(const FfnArgs &a, int RT, const SelectArgs &sa, const Gr
                         uint16_t *hlo, int umax, hipStream_t st) {
     const int slices = a.H / 128 / SPW;
     const int row_bytes = (a.H / 8 + 1) * 16;
-    const int NT = stage_rows(row_bytes);
+    const int NT = stage_rows(row_bytes, RT == 2 ? kStageBytesWide : kStageBytes);
     const size_t lds = (size_t)NT * row_bytes + (size_t)2 * RT * slices * 64 * 16;
     MOE_LAUNCH("ffn_gate_up_sel", (ffn_gate_up_sel<SPW, NPL>), dim3(a.I / (16 * RT), umax),
                dim3(128 * RT * slices), lds, st, a.x, a.H, a.I, a.k, NT, RT, sa, o, hhi, hlo);

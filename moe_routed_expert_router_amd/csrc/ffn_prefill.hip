@@ -82,23 +82,6 @@ __device__ __forceinline__ T lds_ld(const uint8_t *p) {
 // the same idea with 64-byte (gate/up) or 32-byte (down) rows.
 constexpr int kXBytes = kPT * 256;
 
-// N (16 or 4) bytes per lane from rsrc + voff into LDS at wave base +
-// N * lane.  Buffer (not flat) loads, so pending fills do not force the
-// compiler to drain every LDS read before its use.  (Sub-dword sizes would
-// still place lanes 4 bytes apart, so they are not used.)
-template <int N>
-__device__ __forceinline__ void lds_fill(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint8_t *lds_wave_base) {
-    static_assert(N == 16 || N == 4, "fill size");
-    auto *d = (void __attribute__((address_space(3))) *)lds_wave_base;
-    if constexpr (N == 16)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, voff, 0, 0, 0);
-    else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 4, voff, 0, 0, 0);
-}
-
-// Wait for all of this wave's outstanding global loads (LDS fills included).
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
-
 // Double-buffered K loop over S (even) steps: step(cur, nxt, s, nx) computes
 // step s from stage `cur` and starts the fills of step nx into `nxt`.  The
 // last step refills step S - 1 into the idle stage, which nothing reads.
