@@ -93,6 +93,51 @@ __device__ __forceinline__ void split3(const float *v, bf16x8 &hi, bf16x8 &mid, 
     }
 }
 
+// One K step (32 elements) of a wave's operands: the token rows for its two
+// 16-token halves and the router rows for its two 16-expert halves.
+struct RtStep {
+    uint4 xa[2];
+    float4 w[2][2];
+};
+
+__device__ __forceinline__ void rt_load(RtStep &s, const uint16_t *const xr[2], const float *const wrr[2], int kk) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a) s.xa[a] = *reinterpret_cast<const uint4 *>(xr[a] + kk);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        s.w[b][0] = *reinterpret_cast<const float4 *>(wrr[b] + kk);
+        s.w[b][1] = *reinterpret_cast<const float4 *>(wrr[b] + kk + 4);
+    }
+}
+
+__device__ __forceinline__ void rt_compute(const RtStep &s, const bool tv[2], const bool ev[2], f32x4 acc[2][2]) {
+    const uint4 zero4 = {0u, 0u, 0u, 0u};
+    bf16x8 A[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) A[a] = as_bf16x8(tv[a] ? s.xa[a] : zero4);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const float wv[8] = {s.w[b][0].x, s.w[b][0].y, s.w[b][0].z, s.w[b][0].w,
+                             s.w[b][1].x, s.w[b][1].y, s.w[b][1].z, s.w[b][1].w};
+        float wz[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wz[i] = ev[b] ? wv[i] : 0.f;
+        bf16x8 hi, mid, lo;
+        split3(wz, hi, mid, lo);
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+            acc[a][b] = mfma16x16x32(A[a], hi, acc[a][b]);
+            acc[a][b] = mfma16x16x32(A[a], mid, acc[a][b]);
+            acc[a][b] = mfma16x16x32(A[a], lo, acc[a][b]);
+        }
+    }
+}
+
+// The loads run four K steps ahead of the MFMAs (a register ring of four
+// steps, issued unconditionally with the last step repeated at the end), so
+// each wave keeps several round trips in flight instead of one.  (The kernel
+// is still bound by L2 / Infinity Cache traffic: a 64 x 64 block tile reads
+// each router row once per 64 tokens.)
 __global__ __launch_bounds__(256) void route_logits_mfma(
     const uint16_t *__restrict__ x, const float *__restrict__ wr, const float *__restrict__ bias,
     int T, int H, int E, float *__restrict__ z) {
@@ -102,44 +147,32 @@ __global__ __launch_bounds__(256) void route_logits_mfma(
     const int ex0 = blockIdx.x * 64 + (wave & 1) * 32;
     const bool tv[2] = {tok0 + r < T, tok0 + 16 + r < T};
     const bool ev[2] = {ex0 + r < E, ex0 + 16 + r < E};
-    const uint16_t *xr[2] = {x + (size_t)(tv[0] ? tok0 + r : 0) * H,
-                             x + (size_t)(tv[1] ? tok0 + 16 + r : 0) * H};
-    const float *wrr[2] = {wr + (size_t)(ev[0] ? ex0 + r : 0) * H,
-                           wr + (size_t)(ev[1] ? ex0 + 16 + r : 0) * H};
+    const uint16_t *const xr[2] = {x + (size_t)(tv[0] ? tok0 + r : 0) * H + 8 * g,
+                                   x + (size_t)(tv[1] ? tok0 + 16 + r : 0) * H + 8 * g};
+    const float *const wrr[2] = {wr + (size_t)(ev[0] ? ex0 + r : 0) * H + 8 * g,
+                                 wr + (size_t)(ev[1] ? ex0 + 16 + r : 0) * H + 8 * g};
     f32x4 acc[2][2];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const uint4 zero4 = {0u, 0u, 0u, 0u};
-    for (int k0 = 0; k0 < H; k0 += 32) {
-        const int kk = k0 + 8 * g;
-        bf16x8 A[2];
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-            A[a] = as_bf16x8(tv[a] ? *reinterpret_cast<const uint4 *>(xr[a] + kk) : zero4);
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            float wv[8];
-            if (ev[b]) {
-                const float4 w0 = *reinterpret_cast<const float4 *>(wrr[b] + kk);
-                const float4 w1 = *reinterpret_cast<const float4 *>(wrr[b] + kk + 4);
-                wv[0] = w0.x; wv[1] = w0.y; wv[2] = w0.z; wv[3] = w0.w;
-                wv[4] = w1.x; wv[5] = w1.y; wv[6] = w1.z; wv[7] = w1.w;
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) wv[i] = 0.f;
-            }
-            bf16x8 hi, mid, lo;
-            split3(wv, hi, mid, lo);
-#pragma unroll
-            for (int a = 0; a < 2; ++a) {
-                acc[a][b] = mfma16x16x32(A[a], hi, acc[a][b]);
-                acc[a][b] = mfma16x16x32(A[a], mid, acc[a][b]);
-                acc[a][b] = mfma16x16x32(A[a], lo, acc[a][b]);
-            }
-        }
+    const int last = H - 32;   // H is a multiple of 128
+    RtStep s0, s1, s2, s3;
+    rt_load(s0, xr, wrr, 0);
+    rt_load(s1, xr, wrr, 32);
+    rt_load(s2, xr, wrr, 64);
+    rt_load(s3, xr, wrr, 96);
+    for (int k0 = 0; k0 < H; k0 += 128) {
+        const int nk = k0 + 128;
+        rt_compute(s0, tv, ev, acc);
+        rt_load(s0, xr, wrr, nk < H ? nk : last);
+        rt_compute(s1, tv, ev, acc);
+        rt_load(s1, xr, wrr, nk + 32 < H ? nk + 32 : last);
+        rt_compute(s2, tv, ev, acc);
+        rt_load(s2, xr, wrr, nk + 64 < H ? nk + 64 : last);
+        rt_compute(s3, tv, ev, acc);
+        rt_load(s3, xr, wrr, nk + 96 < H ? nk + 96 : last);
     }
     // D[row = token 4*g + i][col = expert r] in lane (r, g), element i
 #pragma unroll
