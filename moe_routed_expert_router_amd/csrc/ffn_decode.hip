@@ -239,8 +239,10 @@ __global__ __launch_bounds__(512) void ffn_gate_up_sel(const uint16_t *__restric
                                                        uint16_t *__restrict__ hlo) {
     extern __shared__ __align__(16) char smem[];
     __shared__ int sid[kFusedSelectPairs], sflag[kFusedSelectPairs], spl[kSmallRouteTokens], sinfo[4];
+    // the residency table borrows the start of the token staging area, which
+    // the selection is done with before any token row arrives
     select_group_block<NPL>(sa, o, blockIdx.x == 0 && blockIdx.y == 0, blockIdx.y,
-                            SelectLds{sid, sflag, spl, sinfo});
+                            SelectLds{sid, sflag, spl, sinfo, reinterpret_cast<int *>(smem)});
     const int n = sinfo[0];
     const uint8_t *base = reinterpret_cast<const uint8_t *>(((uint64_t)(uint32_t)sinfo[3] << 32) | (uint32_t)sinfo[2]);
     if (n == 0 || base == nullptr) return;

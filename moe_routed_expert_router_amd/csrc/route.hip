@@ -252,8 +252,8 @@ hipError_t launch_topk(const float *z, int T, int E, int k, int renorm, int32_t 
 // decode gate/up kernel, which recomputes it per block when no expert is cold).
 template <int NPL>
 __global__ __launch_bounds__(1024) void select_group_small(SelectArgs a, GroupOut o) {
-    __shared__ int sid[1024], sflag[1024], spl[64], sinfo[4];
-    select_group_block<NPL>(a, o, true, -1, SelectLds{sid, sflag, spl, sinfo});
+    __shared__ int sid[1024], sflag[1024], spl[64], sinfo[4], sslot[kMaxExperts];
+    select_group_block<NPL>(a, o, true, -1, SelectLds{sid, sflag, spl, sinfo, sslot});
 }
 
 SelectArgs select_args(const float *z, int T, int k, int renorm, int32_t *ids, float *w, const GroupArgs &a) {

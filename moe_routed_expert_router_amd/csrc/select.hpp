@@ -22,6 +22,7 @@ struct SelectArgs {
 // pair list of the wanted expert, and 4 ints of its summary.
 struct SelectLds {
     int *sid, *sflag, *spl, *sinfo;   // sinfo: [0] pairs n, [1] first position q0, [2..3] blob address
+    int *sslot;                       // [E]: the residency table, copied in while the top-k runs
 };
 
 // Top-k of every token (one wave per token), then the grouping computed from
@@ -32,12 +33,18 @@ struct SelectLds {
 // `o`.  For the distinct expert number `want`, leaves its pair count, first
 // position and blob address in s.sinfo and its pairs, in order, in s.spl
 // (count 0 if there is no such expert).  Every thread of the block calls it.
+// Needs E <= 2 * blockDim.x.
 template <int NPL>
 __device__ __forceinline__ void select_group_block(const SelectArgs &a, const GroupOut &o, bool publish, int want,
                                                    const SelectLds &s) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
-    const int k = a.k;
+    const int k = a.k, bd = blockDim.x;
     if (tid == 0) s.sinfo[0] = 0;
+    // the residency entries are requested before the logits and land in LDS
+    // after the top-k, so looking up the picked experts' entries costs no
+    // round trip of its own
+    const int sl0 = a.slot[tid < a.E ? tid : 0];
+    const int sl1 = a.slot[tid + bd < a.E ? tid + bd : 0];
     for (int t = wave; t < a.T; t += nwaves) {
         int pe;
         float pw;
@@ -50,6 +57,8 @@ __device__ __forceinline__ void select_group_block(const SelectArgs &a, const Gr
             }
         }
     }
+    if (tid < a.E) s.sslot[tid] = sl0;
+    if (tid + bd < a.E) s.sslot[tid + bd] = sl1;
     __syncthreads();
     const int P = a.T * k;
     int e = 0, lt = 0, eqb = 0, cnt = 0, flag = 0;
@@ -64,7 +73,7 @@ __device__ __forceinline__ void select_group_block(const SelectArgs &a, const Gr
         }
         if (eqb == 0) {   // first pair of its expert: 1 first, 2 cold, 4 unusable
             bool ok, cold;
-            addr = expert_address(a.slot[e], a.n_hot, a.n_cold, a.hot_base, a.scratch, a.blob_bytes, &ok, &cold);
+            addr = expert_address(s.sslot[e], a.n_hot, a.n_cold, a.hot_base, a.scratch, a.blob_bytes, &ok, &cold);
             flag = 1 | ((ok && cold) ? 2 : 0) | (ok ? 0 : 4);
         }
         s.sflag[tid] = flag;
