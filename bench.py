@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "routed-expert layer tokens/s + achieved HBM & host-link GB/s at batch 1/8/32"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFS = 2500.0      # MI355X dense bf16 matrix cores, 2.5 PFLOP/s
+DOWN_COMBINE_MAX_PAIRS = 8       # T*k up to which the library fuses the down projection and the combine
 LINK_PEAK_GBS = 64.0             # PCIe Gen5 x16, one direction
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -182,7 +183,10 @@ def layer_bytes(layer_picks) -> dict:
         T = ids.shape[0]
         P = T * k
         gu.append(U * w13 + T * H * 2 + P * I * 4)           # + x read, h (hi+lo) write
-        dn.append(U * w2 + P * I * 4 + P * H * 4)            # + h read, y write
+        if P <= DOWN_COMBINE_MAX_PAIRS:                      # fused down + combine: + h read, out write
+            dn.append(U * w2 + P * I * 4 + T * H * 4)
+        else:                                                # + h read, y write
+            dn.append(U * w2 + P * I * 4 + P * H * 4)
         cold_bytes.append(sum(1 for e in np.unique(ids) if L.slot_np[e] < 0) * L.B)
         uniq.append(U)
     return {"gate_up": float(np.mean(gu)), "down": float(np.mean(dn)),
