@@ -51,6 +51,14 @@ class MoeResidency(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run python moe_routed_expert_router_amd/build.py")
+    # One HIP runtime per process.  torch ships its own copy of the runtime
+    # (same soname as the system one this library links); loaded first, it
+    # also serves this library.  The other order would put two runtimes in the
+    # process, and torch's device memory would be unknown to the library's.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     P = c_void_p
     sig = {

@@ -243,6 +243,15 @@ __device__ __forceinline__ void fill_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Workgroup barrier over LDS only: waits for this wave's LDS operations, not
+// for its outstanding global loads (no LDS fill may be pending).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt(63): no wait on loads
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
     return __builtin_bit_cast(bf16x8, v);
 }

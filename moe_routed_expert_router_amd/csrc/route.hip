@@ -72,122 +72,199 @@ __global__ __launch_bounds__(256) void route_logits_small(const uint16_t *__rest
 }
 
 // ---------------------------------------------------------------------------
-// Prefill-size logits (T > 32): MFMA GEMM on 16x16x32 bf16 tiles.  x is bf16
-// already; each fp32 router weight is split into three bf16 terms (hi + mid +
-// lo carry 24 significant bits), so the three products per term are exact in
-// fp32 and only the fp32 accumulation rounds.  A wave owns a 32-token x
-// 32-expert tile; a 256-thread block 64 x 64.
+// An fp32 value as three bf16 terms hi + mid + lo (24 significant bits, so
+// hi + mid + lo == v for normal v): a product with a bf16 value is then three
+// products that are exact in fp32.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void split3(const float *v, bf16x8 &hi, bf16x8 &mid, bf16x8 &lo) {
+    // native round-to-nearest-even conversions (one instruction per two
+    // values); each remainder is exact in fp32, whatever the rounding
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const float a = v[i];
-        const uint32_t h = f32_to_bf16_bits(a);
-        const float r1 = a - __uint_as_float(h << 16);
-        const uint32_t m = f32_to_bf16_bits(r1);
-        const float r2 = r1 - __uint_as_float(m << 16);
-        const uint32_t l = f32_to_bf16_bits(r2);
-        hi[i] = __builtin_bit_cast(__bf16, (uint16_t)h);
-        mid[i] = __builtin_bit_cast(__bf16, (uint16_t)m);
-        lo[i] = __builtin_bit_cast(__bf16, (uint16_t)l);
+        const __bf16 h = (__bf16)v[i];
+        const float r1 = v[i] - (float)h;
+        const __bf16 m = (__bf16)r1;
+        const float r2 = r1 - (float)m;
+        hi[i] = h;
+        mid[i] = m;
+        lo[i] = (__bf16)r2;
     }
 }
 
-// One K step (32 elements) of a wave's operands: the token rows for its two
-// 16-token halves and the router rows for its two 16-expert halves.
-struct RtStep {
-    uint4 xa[2];
-    float4 w[2][2];
-};
+// ---------------------------------------------------------------------------
+// Prefill-size logits as an LDS-tiled GEMM on 32x32x16 bf16 MFMAs (on gfx950
+// the 32x32 form issues twice the flops per cycle of the 16x16 one).  Same
+// exact-product scheme: x is bf16, each fp32 router weight is split into
+// three bf16 terms and only the fp32 accumulation rounds.  A block computes
+// BT tokens (128, or 64 for at most kRgSmallT tokens, giving more blocks) x
+// 64 experts.  Per K step of 32 it copies the token rows and the fp32 router
+// rows straight into LDS (a ring of four stages, three steps ahead: one
+// step's compute is far shorter than an L2 round trip), splits the router
+// rows once for the whole block into three bf16 planes (native bf16
+// converts), then each wave runs a 32-expert x BT/2-token tile from LDS.
+// Every block of a token tile sits on the same XCD (consecutive blocks go to
+// consecutive XCDs), so the tile's token rows come into that XCD's L2 once
+// for all the expert tiles.  (A wave that reads its operands from global
+// memory and splits the router rows itself re-reads every router row once
+// per 64 tokens and repeats each split 256 times: L2 / Infinity Cache
+// traffic and VALU work that this layout removes.)
+constexpr int kRgE = 64, kRgK = 32;               // experts per block, K step
+constexpr int kRgW = kRgE * kRgK * 4;             // fp32 router rows per stage: 128 B each
+constexpr int kRgPlane = kRgE * kRgK * 2;         // one bf16 plane of the split rows: 64 B each
+constexpr int kRgSmallT = 4096;                   // up to this many tokens, 64-token blocks (more of them)
 
-__device__ __forceinline__ void rt_load(RtStep &s, const uint16_t *const xr[2], const float *const wrr[2], int kk) {
+// LDS rows of 64 bytes hold their four 16-byte chunks swizzled: chunk k of
+// row c sits in slot k ^ (c & 3).
+__device__ __forceinline__ int rg_slot(int c, int k) { return c * 64 + 16 * (k ^ (c & 3)); }
+
+// grid 8 * expert tiles * ceil(token tiles / 8); 256 threads.  H % 32 == 0,
+// T * H * 2 and E * H * 4 below 2^32 (32-bit fill offsets).
+template <int BT>
+__global__ __launch_bounds__(256) void route_logits_gemm(const uint16_t *__restrict__ x, const float *__restrict__ wr,
+                                                         const float *__restrict__ bias, int T, int H, int E,
+                                                         float *__restrict__ z) {
+    // four separate stage arrays, used with fixed roles per unrolled step,
+    // so the compiler can tell a fill's destination from the stage being read
+    // (a computed stage index would make it drain every fill before each read)
+    constexpr int kRgX = BT * kRgK * 2;   // token rows per stage: 64 B each
+    constexpr int kRgStage = kRgX + kRgW;
+    __shared__ __align__(16) uint8_t st0[kRgStage];
+    __shared__ __align__(16) uint8_t st1[kRgStage];
+    __shared__ __align__(16) uint8_t st2[kRgStage];
+    __shared__ __align__(16) uint8_t st3[kRgStage];
+    __shared__ __align__(16) uint8_t sp[3 * kRgPlane];
+    const int net = (E + kRgE - 1) / kRgE, ntt = (T + BT - 1) / BT;
+    const int b = blockIdx.x, xcd = b & 7, rest = b >> 3;
+    const int et = rest % net, tt = (rest / net) * 8 + xcd;
+    if (tt >= ntt) return;
+    const int tok0 = tt * BT, ex0 = et * kRgE;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lc = lane & 31, h = lane >> 5;
+
+    // fills of this wave (byte offsets; a step adds its K offset): token rows
+    // 16 f .. +15 and router rows 8 f .. +7 for f = 2 wave, 2 wave + 1; rows
+    // past T or E repeat a valid row (their results are never stored)
+    const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(x, (uint32_t)((size_t)T * H * 2));
+    const __amdgpu_buffer_rsrc_t wrs = buffer_rsrc(wr, (uint32_t)((size_t)E * H * 4));
+    constexpr int XF = BT / 64;   // token-row fills per wave and step
+    uint32_t xsrc[XF], wsrc[2];
 #pragma unroll
-    for (int a = 0; a < 2; ++a) s.xa[a] = *reinterpret_cast<const uint4 *>(xr[a] + kk);
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        s.w[b][0] = *reinterpret_cast<const float4 *>(wrr[b] + kk);
-        s.w[b][1] = *reinterpret_cast<const float4 *>(wrr[b] + kk + 4);
+    for (int j = 0; j < XF; ++j) {
+        const int f = XF * wave + j;
+        const int c = 16 * f + (lane >> 2), k = (lane & 3) ^ (c & 3);
+        const int t = tok0 + c < T ? tok0 + c : T - 1;
+        xsrc[j] = ((uint32_t)t * (uint32_t)H + 8 * k) * 2;
     }
-}
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int f = 2 * wave + j;
+        const int er = 8 * f + (lane >> 3), e = ex0 + er < E ? ex0 + er : E - 1;
+        wsrc[j] = ((uint32_t)e * (uint32_t)H + 4 * (lane & 7)) * 4;
+    }
+    auto fill = [&](uint8_t *st, int k0) {
+#pragma unroll
+        for (int j = 0; j < XF; ++j) lds_fill<16>(xrs, xsrc[j] + k0 * 2, st + (XF * wave + j) * 1024);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) lds_fill<16>(wrs, wsrc[j] + k0 * 4, st + kRgX + (2 * wave + j) * 1024);
+    };
 
-__device__ __forceinline__ void rt_compute(const RtStep &s, const bool tv[2], const bool ev[2], f32x4 acc[2][2]) {
-    const uint4 zero4 = {0u, 0u, 0u, 0u};
-    bf16x8 A[2];
+    // split: thread tid converts router row tid >> 2, elements 8 (tid & 3) .. +7
+    const int se = tid >> 2, sk = tid & 3;
+    // operand reads of this wave: experts 32 (wave & 1) + lc, tokens
+    // (BT / 2) (wave >> 1) + 32 b + lc for its NB column tiles b
+    constexpr int NB = BT / 64;
+    const int ea = 32 * (wave & 1) + lc, tb0 = (BT / 2) * (wave >> 1) + lc;
+    int aoff[2], boff[NB][2];
 #pragma unroll
-    for (int a = 0; a < 2; ++a) A[a] = as_bf16x8(tv[a] ? s.xa[a] : zero4);
+    for (int q = 0; q < 2; ++q) {
+        aoff[q] = rg_slot(ea, 2 * q + h);
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        const float wv[8] = {s.w[b][0].x, s.w[b][0].y, s.w[b][0].z, s.w[b][0].w,
-                             s.w[b][1].x, s.w[b][1].y, s.w[b][1].z, s.w[b][1].w};
-        float wz[8];
+        for (int bb = 0; bb < NB; ++bb) boff[bb][q] = rg_slot(tb0 + 32 * bb, 2 * q + h);
+    }
+    f32x16 acc[NB];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) wz[i] = ev[b] ? wv[i] : 0.f;
-        bf16x8 hi, mid, lo;
-        split3(wz, hi, mid, lo);
+    for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
-        for (int a = 0; a < 2; ++a) {
-            acc[a][b] = mfma16x16x32(A[a], hi, acc[a][b]);
-            acc[a][b] = mfma16x16x32(A[a], mid, acc[a][b]);
-            acc[a][b] = mfma16x16x32(A[a], lo, acc[a][b]);
+        for (int i = 0; i < 16; ++i) acc[bb][i] = 0.f;
+
+    // the bias of this lane's 16 experts, requested now and used after the K loop
+    float bv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int e = ex0 + 32 * (wave & 1) + 8 * (i / 4) + 4 * h + i % 4;
+        bv[i] = (bias != nullptr && e < E) ? bias[e] : 0.0f;
+    }
+    const int S = H / kRgK;   // a multiple of 4 (H % 128 == 0)
+    // Step s computes from stage s % 4 and fills step s + 3 into the stage of
+    // step s - 1 (steps past the end refill the last one into a stage that
+    // nothing reads).
+    auto step = [&](const uint8_t *cur, uint8_t *nxt, int s) {
+        // this wave's fills of step s are in (the later two steps' 4 fills
+        // each may stay in flight); after the barrier everyone's are, and
+        // every wave is done with step s - 1, whose stage `nxt` is
+        fill_barrier<2 * (XF + 2)>();
+        fill(nxt, (s + 3 < S ? s + 3 : S - 1) * kRgK);
+        {
+            const float4 *src = reinterpret_cast<const float4 *>(cur + kRgX + se * 128 + 32 * sk);
+            const float4 v0 = src[0], v1 = src[1];
+            const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            bf16x8 hi, mid, lo;
+            split3(v, hi, mid, lo);
+            const int o = rg_slot(se, sk);
+            *reinterpret_cast<bf16x8 *>(sp + o) = hi;
+            *reinterpret_cast<bf16x8 *>(sp + kRgPlane + o) = mid;
+            *reinterpret_cast<bf16x8 *>(sp + 2 * kRgPlane + o) = lo;
+        }
+        lds_barrier();
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            bf16x8 a[3], bt[NB];
+#pragma unroll
+            for (int pl = 0; pl < 3; ++pl) a[pl] = *reinterpret_cast<const bf16x8 *>(sp + pl * kRgPlane + aoff[q]);
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb) bt[bb] = *reinterpret_cast<const bf16x8 *>(cur + boff[bb][q]);
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+                for (int pl = 0; pl < 3; ++pl) acc[bb] = mfma32x32x16(a[pl], bt[bb], acc[bb]);
+        }
+    };
+    fill(st0, 0);
+    fill(st1, (1 < S ? 1 : S - 1) * kRgK);
+    fill(st2, (2 < S ? 2 : S - 1) * kRgK);
+    for (int s = 0; s < S; s += 4) {
+        step(st0, st3, s);
+        step(st1, st0, s + 1);
+        step(st2, st1, s + 2);
+        step(st3, st2, s + 3);
+    }
+
+    // lane (lc, h), element i: expert 8 (i / 4) + 4 h + i % 4 of the wave's 32,
+    // token lc of its column tile bb
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+        const int t = tok0 + tb0 + 32 * bb;
+        if (t >= T) continue;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int e = ex0 + 32 * (wave & 1) + 8 * (i / 4) + 4 * h + i % 4;
+            if (e < E) z[(size_t)t * E + e] = acc[bb][i] + bv[i];
         }
     }
 }
 
-// The loads run four K steps ahead of the MFMAs (a register ring of four
-// steps, issued unconditionally with the last step repeated at the end), so
-// each wave keeps several round trips in flight instead of one.  (The kernel
-// is still bound by L2 / Infinity Cache traffic: a 64 x 64 block tile reads
-// each router row once per 64 tokens.)
-__global__ __launch_bounds__(256) void route_logits_mfma(
-    const uint16_t *__restrict__ x, const float *__restrict__ wr, const float *__restrict__ bias,
-    int T, int H, int E, float *__restrict__ z) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int r = lane & 15, g = lane >> 4;
-    const int tok0 = blockIdx.y * 64 + (wave >> 1) * 32;
-    const int ex0 = blockIdx.x * 64 + (wave & 1) * 32;
-    const bool tv[2] = {tok0 + r < T, tok0 + 16 + r < T};
-    const bool ev[2] = {ex0 + r < E, ex0 + 16 + r < E};
-    const uint16_t *const xr[2] = {x + (size_t)(tv[0] ? tok0 + r : 0) * H + 8 * g,
-                                   x + (size_t)(tv[1] ? tok0 + 16 + r : 0) * H + 8 * g};
-    const float *const wrr[2] = {wr + (size_t)(ev[0] ? ex0 + r : 0) * H + 8 * g,
-                                 wr + (size_t)(ev[1] ? ex0 + 16 + r : 0) * H + 8 * g};
-    f32x4 acc[2][2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int last = H - 32;   // H is a multiple of 128
-    RtStep s0, s1, s2, s3;
-    rt_load(s0, xr, wrr, 0);
-    rt_load(s1, xr, wrr, 32);
-    rt_load(s2, xr, wrr, 64);
-    rt_load(s3, xr, wrr, 96);
-    for (int k0 = 0; k0 < H; k0 += 128) {
-        const int nk = k0 + 128;
-        rt_compute(s0, tv, ev, acc);
-        rt_load(s0, xr, wrr, nk < H ? nk : last);
-        rt_compute(s1, tv, ev, acc);
-        rt_load(s1, xr, wrr, nk + 32 < H ? nk + 32 : last);
-        rt_compute(s2, tv, ev, acc);
-        rt_load(s2, xr, wrr, nk + 64 < H ? nk + 64 : last);
-        rt_compute(s3, tv, ev, acc);
-        rt_load(s3, xr, wrr, nk + 96 < H ? nk + 96 : last);
+hipError_t launch_route_logits_gemm(const uint16_t *x, const float *wr, const float *bias, int T, int H, int E,
+                                    float *z, hipStream_t st) {
+    const int net = (E + kRgE - 1) / kRgE;
+    if (T <= kRgSmallT) {
+        const int ntt = (T + 63) / 64;
+        MOE_LAUNCH("route_logits_gemm", route_logits_gemm<64>, dim3(8 * net * ((ntt + 7) / 8)), dim3(256), 0, st, x,
+                   wr, bias, T, H, E, z);
+    } else {
+        const int ntt = (T + 127) / 128;
+        MOE_LAUNCH("route_logits_gemm", route_logits_gemm<128>, dim3(8 * net * ((ntt + 7) / 8)), dim3(256), 0, st, x,
+                   wr, bias, T, H, E, z);
     }
-    // D[row = token 4*g + i][col = expert r] in lane (r, g), element i
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        const int e = ex0 + 16 * b + r;
-        if (e >= E) continue;
-        const float bb = bias ? bias[e] : 0.0f;
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = tok0 + 16 * a + 4 * g + i;
-                if (t < T) z[(size_t)t * E + e] = acc[a][b][i] + bb;
-            }
-    }
+    return hipGetLastError();
 }
 
 hipError_t launch_route_logits(const uint16_t *x, const float *wr, const float *bias,
@@ -206,11 +283,9 @@ hipError_t launch_route_logits(const uint16_t *x, const float *wr, const float *
         else if (nc <= 16)
             MOE_LAUNCH("route_logits_small", route_logits_small<16>, g, b, 0, st, x, wr, bias, T, H, E, z);
         else
-            MOE_LAUNCH("route_logits_mfma", route_logits_mfma, dim3((E + 63) / 64, (T + 63) / 64), dim3(256), 0,
-                       st, x, wr, bias, T, H, E, z);
+            return launch_route_logits_gemm(x, wr, bias, T, H, E, z, st);
     } else {
-        MOE_LAUNCH("route_logits_mfma", route_logits_mfma, dim3((E + 63) / 64, (T + 63) / 64), dim3(256), 0, st,
-                   x, wr, bias, T, H, E, z);
+        return launch_route_logits_gemm(x, wr, bias, T, H, E, z, st);
     }
     return hipGetLastError();
 }
