@@ -61,6 +61,67 @@ __device__ __forceinline__ void select_group_block(const SelectArgs &a, const Gr
     if (tid + bd < a.E) s.sslot[tid + bd] = sl1;
     __syncthreads();
     const int P = a.T * k;
+    if (P <= 64) {
+        // One wave groups the pairs, lane p holding pair p; the other pairs'
+        // values come by lane reads and the counts by ballots, so no
+        // block-wide count reduction (two barriers each) is needed.
+        if (wave == 0) {
+            const bool act = lane < P;
+            const int e = s.sid[act ? lane : 0];
+            int lt = 0, eqb = 0, cnt = 0;
+            for (int q = 0; q < P; ++q) {
+                const int eq = __builtin_amdgcn_readlane(e, q);
+                lt += eq < e;
+                cnt += eq == e;
+                eqb += (eq == e) & (q < lane);
+            }
+            int flag = 0;
+            uint64_t addr = 0;
+            if (act && eqb == 0) {   // first pair of its expert: 1 first, 2 cold, 4 unusable
+                bool ok, cold;
+                addr = expert_address(s.sslot[e], a.n_hot, a.n_cold, a.hot_base, a.scratch, a.blob_bytes, &ok, &cold);
+                flag = 1 | ((ok && cold) ? 2 : 0) | (ok ? 0 : 4);
+            }
+            if (act && publish) o.plist[lt + eqb] = lane;
+            const int nu = __popcll(__ballot(flag & 1)), nc = __popcll(__ballot(flag & 2));
+            const int nb = __popcll(__ballot(flag & 4));
+            int ui = 0, ci = 0;
+            for (int q = 0; q < P; ++q) {
+                const int fq = __builtin_amdgcn_readlane(flag, q), less = __builtin_amdgcn_readlane(e, q) < e;
+                ui += (fq & 1) & less;
+                ci += ((fq >> 1) & 1) & less;
+            }
+            if (act && publish && (flag & 1)) {
+                o.uniq[ui] = e;
+                o.ucnt[ui] = cnt;
+                o.uoff[ui] = lt;
+                o.uptr[ui] = addr;
+                o.ucold[ui] = (flag >> 1) & 1;
+                if (flag & 2) {
+                    o.cold[ci] = e;
+                    o.cu[ci] = ui;
+                }
+            }
+            if (act && ui == want) {
+                s.spl[eqb] = lane;
+                if (flag & 1) {
+                    s.sinfo[0] = cnt;
+                    s.sinfo[1] = lt;
+                    s.sinfo[2] = (int)(uint32_t)addr;
+                    s.sinfo[3] = (int)(uint32_t)(addr >> 32);
+                }
+            }
+            if (publish && lane == 0) {
+                o.nuniq[0] = nu;
+                o.nuniq[1] = nc;
+                o.status[0] = 0;
+                o.status[1] = nb;
+                o.uoff[nu] = P;
+            }
+        }
+        __syncthreads();
+        return;
+    }
     int e = 0, lt = 0, eqb = 0, cnt = 0, flag = 0;
     uint64_t addr = 0;
     if (tid < P) {
