@@ -44,6 +44,8 @@ __global__ __launch_bounds__(kChunk) void group_hist(const int32_t *__restrict__
     for (int i = tid; i <= E; i += kChunk) row[i] = cnt[i];
 }
 
+constexpr int kScanBatch = 16;   // chunk counts loaded together per thread
+
 __global__ __launch_bounds__(1024) void group_scan(int nchunks, int E, const int32_t *__restrict__ slot,
                                                    int n_hot, int n_cold, const uint8_t *hot_base,
                                                    const uint8_t *scratch, size_t blob_bytes,
@@ -58,12 +60,17 @@ __global__ __launch_bounds__(1024) void group_scan(int nchunks, int E, const int
     const int e = threadIdx.x;
     for (int i = e; i < WsLayout::kSyncWords; i += 1024) sync[i] = 0;
     const int stride = E + 1;
+    // the expert's pair count over all chunks, kScanBatch loads in flight at
+    // a time (one dependent round trip per chunk would cost ~0.5 us each)
     int total = 0;
     if (e < E) {
-        for (int c = 0; c < nchunks; ++c) {
-            const int h = hist[(size_t)c * stride + e];
-            hist[(size_t)c * stride + e] = total;
-            total += h;
+        for (int c0 = 0; c0 < nchunks; c0 += kScanBatch) {
+            int v[kScanBatch];
+#pragma unroll
+            for (int j = 0; j < kScanBatch; ++j)
+                v[j] = c0 + j < nchunks ? hist[(size_t)(c0 + j) * stride + e] : 0;
+#pragma unroll
+            for (int j = 0; j < kScanBatch; ++j) total += v[j];
         }
     }
     const bool is_exp = e < E;
@@ -100,11 +107,29 @@ __global__ __launch_bounds__(1024) void group_scan(int nchunks, int E, const int
             cold[ci] = e;
             cu[ci] = ui;
         }
-        for (int c = 0; c < nchunks; ++c) hist[(size_t)c * stride + e] += off;
+        // each chunk's base for the expert: its global offset plus the pairs
+        // of the earlier chunks
+        int run = off;
+        for (int c0 = 0; c0 < nchunks; c0 += kScanBatch) {
+            int v[kScanBatch];
+#pragma unroll
+            for (int j = 0; j < kScanBatch; ++j)
+                v[j] = c0 + j < nchunks ? hist[(size_t)(c0 + j) * stride + e] : 0;
+#pragma unroll
+            for (int j = 0; j < kScanBatch; ++j)
+                if (c0 + j < nchunks) {
+                    hist[(size_t)(c0 + j) * stride + e] = run;
+                    run += v[j];
+                }
+        }
+    }
+    int bad = 0;   // out-of-range pair count, over the chunks in parallel
+    for (int c0 = 0; c0 < nchunks; c0 += 1024) {
+        int part;
+        block_exscan1024(c0 + e < nchunks ? hist[(size_t)(c0 + e) * stride + E] : 0, lds, &part);
+        bad += part;
     }
     if (e == 0) {
-        int bad = 0;   // out-of-range pair count
-        for (int c = 0; c < nchunks; ++c) bad += hist[(size_t)c * stride + E];
         status[0] = bad;
         nuniq[0] = nu;
         nuniq[1] = nc;
