@@ -339,6 +339,65 @@ def measure_ffn_batches(batches=(1, 8, 32), layers: int = 4, reps: int = 10) -> 
     return out
 
 
+def measure_direct_read(batches=(1, 8, 32), layers: int = 4, reps: int = 8) -> dict:
+    """Gather-then-compute against direct read (the FFN reads the picked cold
+    experts in place from pinned host memory) for hot/cold decode layers
+    (255 hot / 129 cold, Zipf routing) at each batch size: the whole layer
+    per forward, `layers` layers rotating (each with its own cold pool, so
+    no forward finds its host bytes in a GPU cache), replayed from a HIP
+    graph per mode, event-timed."""
+    import torch
+    from synth import gen
+    from tests.gpu_setup import Layer
+    wl = gen.workload("hotcold8")
+    cal = gen.load_calibration()
+    out = {}
+    for T in batches:
+        G, D = [], []
+        try:
+            for l in range(layers):
+                G.append(Layer(wl, layer=l, T=T, cal=cal))
+                D.append(Layer(wl, layer=l, T=T, cal=cal, host=G[-1].host, direct=True))
+            us = {}
+            for name, Ls in (("gather", G), ("direct", D)):
+                s = torch.cuda.Stream()
+                s.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(s):
+                    for L in Ls:
+                        L.forward(stream=s.cuda_stream)
+                s.synchronize()
+                graph = torch.cuda.CUDAGraph()   # the layers' launches, replayed without host overhead
+                with torch.cuda.graph(graph, stream=s, capture_error_mode="relaxed"):
+                    for L in Ls:
+                        L.forward(stream=s.cuda_stream)
+                graph.replay()
+                torch.cuda.synchronize()
+                t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                t0.record()
+                for _ in range(reps):
+                    graph.replay()
+                t1.record()
+                torch.cuda.synchronize()
+                us[name] = t0.elapsed_time(t1) * 1e3 / (reps * layers)
+                del graph
+            cold = float(np.mean([sum(1 for e in np.unique(L.ids.cpu().numpy()) if L.slot_np[e] < 0) * L.B
+                                  for L in D]))
+            out[f"batch{T}"] = {
+                "tokens": T, "cold_bytes_per_forward": int(cold),
+                "gather_us": round(us["gather"], 2), "direct_us": round(us["direct"], 2),
+                "gather_tokens_per_s": round(T / (us["gather"] * 1e-6), 1),
+                "direct_tokens_per_s": round(T / (us["direct"] * 1e-6), 1),
+                "direct_over_gather": round(us["gather"] / us["direct"], 3)}
+            log(f"[bench] direct read batch {T}: gather {us['gather']:.1f} us, direct {us['direct']:.1f} us, "
+                f"{cold / 1e6:.1f} MB cold per forward")
+        finally:
+            for L in D + G:
+                L.close()
+            del G, D
+            torch.cuda.empty_cache()
+    return out
+
+
 def measure_stack(name: str, steps: int, warmup: int, use_graph: bool) -> dict:
     """Whole decode steps of a multi-layer workload (every layer in order on
     one stream, one shared cold scratch); None if it does not fit the GPU."""
@@ -425,6 +484,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batch8", action="store_true", help="skip the batch-8 hot/cold secondary figures")
+    ap.add_argument("--no-direct-read", action="store_true",
+                    help="skip the gather vs direct-read comparison (hot/cold decode, batch 1/8/32)")
     ap.add_argument("--no-ffn-batches", action="store_true",
                     help="skip the standalone grouped-FFN figures at batch 1/8/32")
     ap.add_argument("--no-step40", action="store_true", help="skip the 40-layer batch-32 secondary figures")
@@ -520,6 +581,10 @@ def main():
         w8.close()
         del w8
         torch.cuda.empty_cache()
+
+    if not a.no_direct_read and a.workload == "decode1":
+        log("[bench] secondary: gather-then-compute vs direct read of cold experts (batch 1/8/32)")
+        extra["direct_read"] = measure_direct_read()
 
     if not a.no_ffn_batches and a.workload == "decode1":
         log("[bench] secondary: grouped FFN alone at batch 1/8/32 (all experts resident)")

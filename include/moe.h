@@ -92,7 +92,14 @@ typedef struct {
  *   host_cold device-visible pointer to pinned host memory [n_cold][B]
  *             (moe_host_alloc()); may be NULL when n_cold == 0.
  *   scratch   device [n_cold][B]; the cold experts' HBM slots, which may be
- *             shared by every layer; may be NULL when n_cold == 0. */
+ *             shared by every layer; may be NULL when n_cold == 0.
+ *             scratch == host_cold selects direct read: the FFN reads each
+ *             picked cold expert in place from pinned host memory over the
+ *             host link, and nothing is copied (the pages' mapped / UVA
+ *             alternative to the copy kernel: gracetier write-up, section 1,
+ *             against the row-level UVA offload of the GB300 write-up's
+ *             results table and the mapped W2 plane of the RTX PRO 6000
+ *             write-up, "Five layers made the difference"). */
 typedef struct {
     const int32_t *slot;
     const uint8_t *hot_base;
@@ -163,7 +170,8 @@ moe_status moe_pick_set(const moe_shape *s, int32_t n_tokens, const int32_t *top
  * copied whole, once, from host_cold + c*B to scratch + c*B (c = -slot[e]-1),
  * by a kernel that reads the pinned host memory directly; unpicked slots are
  * not touched.  No host round trip decides what is copied.  With
- * r->n_cold == 0 nothing is enqueued. */
+ * r->n_cold == 0, or in direct read (scratch == host_cold), nothing is
+ * enqueued. */
 moe_status moe_gather_cold(const moe_shape *s, int32_t n_tokens, const int32_t *topk_ids,
                            const moe_residency *r, void *ws, size_t ws_bytes, void *stream);
 
@@ -180,7 +188,8 @@ moe_status moe_expert_ffn(const moe_shape *s, int32_t n_tokens, const uint16_t *
                           void *ws, size_t ws_bytes, void *stream);
 
 /* The whole layer: moe_route, then the pick set, the cold gather
- * (skipped when r->n_cold == 0) and the grouped FFN with the combine, ordered
+ * (skipped when r->n_cold == 0 or in direct read) and the grouped FFN with
+ * the combine, ordered
  * on `stream`: the call returns with everything enqueued after work already
  * on `stream` and later work on `stream` sees the finished layer.  At decode
  * sizes with cold experts, the gather runs on a library-owned side stream of

@@ -110,6 +110,10 @@ moe_status check_residency(const moe_shape *s, const moe_residency *r) {
     return MOE_OK;
 }
 
+// Direct read: the cold experts are read in place from pinned host memory
+// (the caller passed the host pool as the scratch), so nothing is gathered.
+bool direct_read(const moe_residency *r) { return r->n_cold > 0 && r->scratch == r->host_cold; }
+
 moe_status hip_status(hipError_t e, const char *what) {
     if (e != hipSuccess) {
         (void)hipGetLastError();   // reported here: do not leave it for the caller's next HIP call
@@ -336,7 +340,7 @@ moe_status moe_gather_cold(const moe_shape *s, int32_t T, const int32_t *topk_id
     TRY(check_shape(s));
     TRY(check_tokens(T));
     TRY(check_residency(s, r));
-    if (T == 0 || r->n_cold == 0) return ok();
+    if (T == 0 || r->n_cold == 0 || direct_read(r)) return ok();
     TRY(check_ptr(topk_ids, (size_t)T * s->top_k * 4, 4, "topk_ids"));
     TRY(check_ws(s, T, ws, ws_bytes));
     const moe::WsLayout L = moe::WsLayout::make(s->hidden, s->inter, s->n_experts, s->top_k, T);
@@ -391,7 +395,8 @@ moe_status moe_layer_forward(const moe_shape *s, int32_t T, const uint16_t *x, c
     float *z = reinterpret_cast<float *>(w + L.logits);
     const moe::GroupArgs g = group_args(s, T, topk_ids, r);
     TRY(hip_status(moe::launch_route_logits(x, w_router, bias, T, H, E, z, st), "router logits launch"));
-    if (T <= moe::kSmallRouteTokens && r->n_cold == 0 && moe::ffn_select_fusable(T, k, H, s->inter)) {
+    const bool direct = direct_read(r);
+    if (T <= moe::kSmallRouteTokens && (r->n_cold == 0 || direct) && moe::ffn_select_fusable(T, k, H, s->inter)) {
         // no cold expert to gather: the gate/up kernel selects and groups by itself
         moe::FfnArgs a;
         a.x = x;
@@ -415,7 +420,7 @@ moe_status moe_layer_forward(const moe_shape *s, int32_t T, const uint16_t *x, c
         TRY(hip_status(moe::launch_topk(z, T, E, k, renormalize != 0, topk_ids, topk_w, st), "top-k launch"));
         TRY(hip_status(moe::launch_group(g, w, L, st), "pick-set launch"));
     }
-    if (r->n_cold > 0 && moe::ffn_block_path(T, H, s->inter)) {
+    if (r->n_cold > 0 && !direct && moe::ffn_block_path(T, H, s->inter)) {
         // the hot experts' FFN needs nothing from the gather: it runs on the
         // caller's stream while the side stream copies the cold experts in;
         // the cold experts' FFN and the combine follow the join
@@ -446,7 +451,7 @@ moe_status moe_layer_forward(const moe_shape *s, int32_t T, const uint16_t *x, c
                        "cold ffn launch"));
         return ok();
     }
-    if (r->n_cold > 0)
+    if (r->n_cold > 0 && !direct)
         TRY(hip_status(moe::launch_gather(r->host_cold, r->scratch, g.blob_bytes, r->slot, w, L, st),
                        "gather launch"));
     TRY(enqueue_ffn(s, T, x, topk_ids, topk_w, out_dtype, out, w, L, st));

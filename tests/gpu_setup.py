@@ -51,7 +51,9 @@ class Layer:
 
     def __init__(self, wl: gen.Workload, layer: int = 0, T: int | None = None, scratch=None,
                  all_hot: bool = False, cal: dict | None = None, coherent: bool = False,
-                 hot: list | None = None, host: HostBuffer | None = None):
+                 hot: list | None = None, host: HostBuffer | None = None, direct: bool = False):
+        """direct: cold experts are read in place from the pinned host pool
+        (the residency's scratch is the host pool; nothing is gathered)."""
         self.wl, self.layer = wl, layer
         H, I, E, k = wl.hidden, wl.inter, wl.n_experts, wl.top_k
         self.H, self.I, self.E, self.k = H, I, E, k
@@ -94,10 +96,13 @@ class Layer:
             else:
                 assert host.nbytes == self.n_cold * self.B
                 self.host = host
-            self.scratch = scratch if scratch is not None else torch.empty(
-                (self.n_cold, self.B), dtype=torch.uint8, device=dev)
+            if not direct:
+                self.scratch = scratch if scratch is not None else torch.empty(
+                    (self.n_cold, self.B), dtype=torch.uint8, device=dev)
+        self.direct = direct and self.n_cold > 0
         self.residency = moe.residency(self.slot, self.hot_base if self.n_hot else None,
-                                       self.host.dev if self.host else None, self.scratch,
+                                       self.host.dev if self.host else None,
+                                       self.host.dev if self.direct else self.scratch,
                                        self.n_hot, self.n_cold)
         self.ws = torch.empty(moe.moe_workspace_bytes(self.shape, self.T), dtype=torch.uint8, device=dev)
         self.ids = torch.empty((self.T, k), dtype=torch.int32, device=dev)
