@@ -339,6 +339,96 @@ def measure_ffn_batches(batches=(1, 8, 32), layers: int = 4, reps: int = 10) -> 
     return out
 
 
+def graph_us_per_layer(Ls, reps: int) -> float:
+    """Mean microseconds per layer forward of the layers Ls run in order,
+    captured once in a HIP graph and replayed `reps` times (event-timed, no
+    host launch overhead)."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for L in Ls:
+            L.forward(stream=s.cuda_stream)
+    s.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s, capture_error_mode="relaxed"):
+        for L in Ls:
+            L.forward(stream=s.cuda_stream)
+    graph.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    del graph
+    return t0.elapsed_time(t1) * 1e3 / (reps * len(Ls))
+
+
+def measure_verify(streams=(1, 2, 4, 8, 16), layers: int = 4, reps: int = 8) -> dict:
+    """Speculative-verify decode steps on hot/cold layers (255 resident, 129
+    gathered): S streams x (1 + draft) tokens, draft 5 at 1-4 streams and 1
+    at 5-16, windows correlated so that a 1 + 5 window touches ~3.7x one
+    token's experts.  Per S: us per layer forward (graph replay, `layers`
+    layers rotating, each with its own cold pool), verified tokens/s per
+    layer, distinct experts per window and per forward, cold bytes gathered
+    per forward."""
+    import torch
+    from synth import gen
+    from tests.gpu_setup import HostBuffer, Layer, fill_host_experts
+    wl = gen.workload("hotcold8")
+    cal = gen.load_calibration()
+    rho = gen.load_verify_calibration()["rho"]
+    B = gen.expert_bytes(wl.hidden, wl.inter)
+    out = {}
+    pools = []
+    try:
+        for l in range(layers):   # each layer's cold pool, shared by every stream count
+            hot = set(gen.hot_set(wl.seed, l, cal))
+            cold = [e for e in range(wl.n_experts) if e not in hot]
+            pools.append(HostBuffer(len(cold) * B))
+            fill_host_experts(pools[-1], wl.seed, l, cold, wl.hidden, wl.inter)
+        for S in streams:
+            out[f"streams{S}"] = _verify_point(wl, cal, rho, pools, S, reps)
+    finally:
+        for p in pools:
+            p.close()
+    return out
+
+
+def _verify_point(wl, cal, rho, pools, S, reps):
+    """One stream count of measure_verify (layers borrow the cold pools)."""
+    import torch
+    from synth import gen
+    from tests.gpu_setup import Layer
+    W = gen.verify_window(S)
+    Ls = []
+    try:
+        for l, pool in enumerate(pools):
+            x = gen.verify_tokens_bf16(wl.seed + 100, l, S, W, wl.hidden, rho)
+            Ls.append(Layer(wl, layer=l, cal=cal, x_np=x, host=pool))
+        us = graph_us_per_layer(Ls, reps)
+        ids = [L.ids.cpu().numpy() for L in Ls]
+        win = float(np.mean([len(np.unique(i[s * W:(s + 1) * W])) for i in ids for s in range(S)]))
+        fwd = float(np.mean([len(np.unique(i)) for i in ids]))
+        cold = float(np.mean([sum(1 for e in np.unique(i) if L.slot_np[e] < 0) * L.B
+                              for i, L in zip(ids, Ls)]))
+        T = S * W
+        log(f"[bench] verify {S} streams x {W}: {us:.1f} us/layer, {win:.1f} experts per window "
+            f"({win / wl.top_k:.2f}x one token), {cold / 1e6:.1f} MB cold per forward")
+        return {"tokens": T, "window": W, "us_per_layer": round(us, 2),
+                "verified_tokens_per_s_per_layer": round(T / (us * 1e-6), 1),
+                "distinct_experts_per_window": round(win, 2),
+                "window_over_one_token": round(win / wl.top_k, 3),
+                "distinct_experts_per_forward": round(fwd, 2), "cold_bytes_per_forward": int(cold)}
+    finally:
+        for L in Ls:
+            L.close()
+        del Ls
+        torch.cuda.empty_cache()
+
+
 def measure_direct_read(batches=(1, 8, 32), layers: int = 4, reps: int = 8) -> dict:
     """Gather-then-compute against direct read (the FFN reads the picked cold
     experts in place from pinned host memory) for hot/cold decode layers
@@ -358,28 +448,7 @@ def measure_direct_read(batches=(1, 8, 32), layers: int = 4, reps: int = 8) -> d
             for l in range(layers):
                 G.append(Layer(wl, layer=l, T=T, cal=cal))
                 D.append(Layer(wl, layer=l, T=T, cal=cal, host=G[-1].host, direct=True))
-            us = {}
-            for name, Ls in (("gather", G), ("direct", D)):
-                s = torch.cuda.Stream()
-                s.wait_stream(torch.cuda.current_stream())
-                with torch.cuda.stream(s):
-                    for L in Ls:
-                        L.forward(stream=s.cuda_stream)
-                s.synchronize()
-                graph = torch.cuda.CUDAGraph()   # the layers' launches, replayed without host overhead
-                with torch.cuda.graph(graph, stream=s, capture_error_mode="relaxed"):
-                    for L in Ls:
-                        L.forward(stream=s.cuda_stream)
-                graph.replay()
-                torch.cuda.synchronize()
-                t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                t0.record()
-                for _ in range(reps):
-                    graph.replay()
-                t1.record()
-                torch.cuda.synchronize()
-                us[name] = t0.elapsed_time(t1) * 1e3 / (reps * layers)
-                del graph
+            us = {name: graph_us_per_layer(Ls, reps) for name, Ls in (("gather", G), ("direct", D))}
             cold = float(np.mean([sum(1 for e in np.unique(L.ids.cpu().numpy()) if L.slot_np[e] < 0) * L.B
                                   for L in D]))
             out[f"batch{T}"] = {
@@ -396,6 +465,69 @@ def measure_direct_read(batches=(1, 8, 32), layers: int = 4, reps: int = 8) -> d
             del G, D
             torch.cuda.empty_cache()
     return out
+
+
+def measure_layer_copy(T: int = 32, layers: int = 40, reps: int = 3) -> dict:
+    """Layer-granular copy baseline: the layer's whole expert set (all 384
+    experts, 5.13 GB, kept in pinned host memory as a layer offloader keeps
+    it) copied to HBM before the layer runs, then the layer computed on the
+    copy.  The copy is timed two ways: the gather kernel with every expert
+    picked, and the DMA engines (a plain host -> device tensor copy).  Per-
+    step tokens/s is for `layers` such layers at T tokens each, to set
+    beside the picked-only step of the same shape."""
+    import torch
+    import moe_routed_expert_router_amd as moe
+    from synth import gen
+    from tests.gpu_setup import Layer
+    wl = gen.workload("hotcold8")
+    E, k = wl.n_experts, wl.top_k
+    L = Layer(wl, T=T, hot=[])        # nothing resident: the layer lives on the host
+    try:
+        B = L.B
+        nbytes = E * B
+        Tc = -(-E // k)
+        pad = list(range(E)) + [0] * (Tc * k - E)
+        ids = torch.tensor(pad, dtype=torch.int32, device="cuda").reshape(Tc, k)
+        ws = torch.empty(moe.moe_workspace_bytes(L.shape, Tc), dtype=torch.uint8, device="cuda")
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+        def timed(fn):
+            fn()
+            torch.cuda.synchronize()
+            t0.record()
+            for _ in range(reps):
+                fn()
+            t1.record()
+            torch.cuda.synchronize()
+            return t0.elapsed_time(t1) / reps
+
+        kern_ms = timed(lambda: moe.moe_gather_cold(L.shape, ids, L.residency, ws))
+        same = bool(np.array_equal(L.scratch[:4].cpu().numpy().ravel(), L.host.np[:4 * B]))
+        src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+        dst = L.scratch.view(-1)
+        dma_ms = timed(lambda: dst.copy_(src, non_blocking=True))
+        del src
+        hot = Layer(wl, T=T, all_hot=True)   # the layer computed on its HBM copy
+        try:
+            fwd_ms = timed(lambda: hot.forward())
+        finally:
+            hot.close()
+        copy_ms = min(kern_ms, dma_ms)
+        step_ms = layers * (copy_ms + fwd_ms)
+        res = {"bytes_per_layer": nbytes, "experts": E,
+               "gather_kernel_ms": round(kern_ms, 3), "gather_kernel_GB_per_s": round(nbytes / kern_ms / 1e6, 2),
+               "dma_copy_ms": round(dma_ms, 3), "dma_copy_GB_per_s": round(nbytes / dma_ms / 1e6, 2),
+               "forward_resident_ms": round(fwd_ms, 4), "tokens_per_layer": T, "layers": layers,
+               "ms_per_step": round(step_ms, 2), "tokens_per_s": round(T / (step_ms * 1e-3), 2),
+               "gather_copy_bit_exact": same}
+        log(f"[bench] layer copy: {nbytes / 1e9:.2f} GB per layer, kernel {kern_ms:.1f} ms "
+            f"({nbytes / kern_ms / 1e6:.1f} GB/s), DMA {dma_ms:.1f} ms ({nbytes / dma_ms / 1e6:.1f} GB/s); "
+            f"{layers} layers x {T} tokens: {res['tokens_per_s']} tok/s")
+        return res
+    finally:
+        L.close()
+        del L
+        torch.cuda.empty_cache()
 
 
 def measure_stack(name: str, steps: int, warmup: int, use_graph: bool) -> dict:
@@ -484,6 +616,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batch8", action="store_true", help="skip the batch-8 hot/cold secondary figures")
+    ap.add_argument("--no-verify", action="store_true", help="skip the speculative-verify secondary figures")
+    ap.add_argument("--no-layer-copy", action="store_true",
+                    help="skip the whole-layer cold copy baseline")
     ap.add_argument("--no-direct-read", action="store_true",
                     help="skip the gather vs direct-read comparison (hot/cold decode, batch 1/8/32)")
     ap.add_argument("--no-ffn-batches", action="store_true",
@@ -586,6 +721,14 @@ def main():
         log("[bench] secondary: gather-then-compute vs direct read of cold experts (batch 1/8/32)")
         extra["direct_read"] = measure_direct_read()
 
+    if not a.no_verify and a.workload == "decode1":
+        log("[bench] secondary: speculative-verify steps (streams x (1 + draft), correlated windows)")
+        extra["verify"] = measure_verify()
+
+    if not a.no_layer_copy and a.workload == "decode1":
+        log("[bench] secondary: layer-granular copy baseline (all 384 experts of a layer from the host)")
+        extra["layer_copy"] = measure_layer_copy()
+
     if not a.no_ffn_batches and a.workload == "decode1":
         log("[bench] secondary: grouped FFN alone at batch 1/8/32 (all experts resident)")
         extra["ffn_by_batch"] = measure_ffn_batches()
@@ -593,6 +736,9 @@ def main():
     if not a.no_step40 and a.workload == "decode1":
         log("[bench] secondary: step40 (40 layers, batch 32, 255 hot / 129 cold, shared scratch)")
         extra["step40_batch32"] = measure_stack("step40", 10, 2, not a.no_graph)
+        lc, st = extra.get("layer_copy"), extra["step40_batch32"]
+        if lc and "tokens_per_s" in st:
+            lc["picked_only_over_layer_copy"] = round(st["tokens_per_s"] / lc["tokens_per_s"], 1)
 
     cpu = None
     if not a.no_cpu_baseline:

@@ -12,6 +12,12 @@ module takes for them):
   40 layers sharing it: the "gracetier" write-up, section 1 ("The idea").
 * 98.7% of picks landing on 73% of experts: the GB300 write-up, the
   paragraph on hot/cold doors closed by the hardware.
+* Speculative verify windows: 1 + 5 tokens per stream at 1-4 streams, 1 + 1
+  at 5-16 (the GB300 write-up, its launch-flag table, the speculative-config
+  row); a 1 + 5 window touching 3.7x the distinct experts of one token (the
+  same write-up, the table of what was tried, the speculative-fetching row).
+  Tokens of one window share a common component (correlation rho, fitted to
+  that multiplier with the oracle's router and kept in verify_calibration.json).
 
 Expert weight bytes come from a counter-based 32-bit hash so that the same
 bytes can be produced on the CPU (numpy, for the oracle) and directly in GPU
@@ -34,7 +40,8 @@ __all__ = [
     "stream_keys", "hash_words_np", "expert_sections", "expert_blob",
     "fill_expert_blobs_device", "tokens_bf16", "router_weight", "zipf_prior",
     "load_calibration", "hot_set", "residency_slots", "bf16_round_bits",
-    "CALIBRATION_PATH",
+    "CALIBRATION_PATH", "verify_window", "verify_tokens_bf16", "load_verify_calibration",
+    "VERIFY_CALIBRATION_PATH",
 ]
 
 M32 = 0xFFFFFFFF
@@ -42,6 +49,7 @@ M32 = 0xFFFFFFFF
 # Section tags of the per-expert byte streams and of the Philox streams.
 TAG_W13_NIB, TAG_W13_SCALE, TAG_W2_NIB, TAG_W2_SCALE = 1, 2, 3, 4
 TAG_TOKENS, TAG_ROUTER, TAG_ZIPF_RANK = 5, 6, 7
+TAG_VERIFY_SHARED, TAG_VERIFY_OWN = 8, 9
 
 SCALE_LO, SCALE_N = 123, 5          # e8m0 bytes uniform over 123..127 (2^-4..2^0)
 
@@ -271,11 +279,39 @@ def zipf_prior(seed: int, layer: int, E: int, alpha: float, s: float = 1.1) -> n
     return (-alpha * s * np.log(rank)).astype(np.float32)
 
 
+def verify_window(streams: int) -> int:
+    """Tokens per stream in one verify step: the drafter proposes 5 tokens
+    at 1-4 concurrent streams and 1 at 5-16, and the step checks them with
+    the stream's current token (1 + draft length)."""
+    if not 1 <= streams <= 16:
+        raise ValueError("the draft schedule covers 1..16 streams")
+    return 6 if streams <= 4 else 2
+
+
+def verify_tokens_bf16(seed: int, layer: int, streams: int, window: int, H: int, rho: float) -> np.ndarray:
+    """Verify-step activations, uint16 bf16 bits [streams*window][H], rows
+    stream-major.  Row (s, j) = sqrt(rho) * a_s + sqrt(1 - rho) * n_sj with
+    a_s, n_sj ~ N(0, I) drawn independently: unit variance per element,
+    correlation rho between two tokens of one window, none across windows."""
+    a = _philox(seed, TAG_VERIFY_SHARED, layer).standard_normal((streams, H), dtype=np.float32)
+    n = _philox(seed, TAG_VERIFY_OWN, layer).standard_normal((streams, window, H), dtype=np.float32)
+    x = np.float32(math.sqrt(rho)) * a[:, None, :] + np.float32(math.sqrt(1.0 - rho)) * n
+    return bf16_round_bits(x.reshape(streams * window, H))
+
+
 # ----------------------------- calibration data -----------------------------
 CALIBRATION_PATH = os.path.join(os.path.dirname(__file__), "zipf_calibration.json")
 
 
 def load_calibration(path: str = CALIBRATION_PATH) -> dict:
+    with open(path) as f:
+        return json.load(f)
+
+
+VERIFY_CALIBRATION_PATH = os.path.join(os.path.dirname(__file__), "verify_calibration.json")
+
+
+def load_verify_calibration(path: str = VERIFY_CALIBRATION_PATH) -> dict:
     with open(path) as f:
         return json.load(f)
 

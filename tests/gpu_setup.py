@@ -51,17 +51,19 @@ class Layer:
 
     def __init__(self, wl: gen.Workload, layer: int = 0, T: int | None = None, scratch=None,
                  all_hot: bool = False, cal: dict | None = None, coherent: bool = False,
-                 hot: list | None = None, host: HostBuffer | None = None, direct: bool = False):
+                 hot: list | None = None, host: HostBuffer | None = None, direct: bool = False,
+                 x_np: np.ndarray | None = None):
         """direct: cold experts are read in place from the pinned host pool
-        (the residency's scratch is the host pool; nothing is gathered)."""
+        (the residency's scratch is the host pool; nothing is gathered).
+        x_np: the tokens (uint16 bf16 bits [T][H]) instead of the seeded N(0,1) ones."""
         self.wl, self.layer = wl, layer
         H, I, E, k = wl.hidden, wl.inter, wl.n_experts, wl.top_k
         self.H, self.I, self.E, self.k = H, I, E, k
-        self.T = wl.tokens if T is None else T
+        self.T = (wl.tokens if T is None else T) if x_np is None else x_np.shape[0]
         self.B = gen.expert_bytes(H, I)
         self.shape = moe.shape(H, I, E, k)
         seed = wl.seed
-        self.x_np = gen.tokens_bf16(seed, layer, self.T, H)
+        self.x_np = gen.tokens_bf16(seed, layer, self.T, H) if x_np is None else np.ascontiguousarray(x_np)
         self.wr_np = gen.router_weight(seed, layer, E, H)
         self.bias_np = None
         if wl.zipf:
