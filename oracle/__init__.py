@@ -22,6 +22,11 @@ Modules
   ffn     SwiGLU expert FFN and the weighted top-k combine
   gather  the picked-cold set and the scratch copy
   layer   one whole layer end to end
+  residency  pick counts, decayed scores and the swap rule of the adaptive
+             residency manager; the fingerprint of the byte audit
+
+Offline recipe scripts (they route with the oracle and write the seeded input
+recipe's data under synth/): calibrate_zipf, calibrate_verify.
 
 Every function here is pinned by tests against something other than itself
 (format tables, brute force on tiny inputs, closed forms, invariants); none is
