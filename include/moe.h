@@ -203,6 +203,73 @@ moe_status moe_layer_forward(const moe_shape *s, int32_t n_tokens, const uint16_
                              int32_t out_dtype, void *out,
                              void *ws, size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Adaptive residency and the byte audit.  The gracetier write-up: between
+ * decode steps a manager swaps experts that are being picked often into the
+ * hot set and moves quiet ones out (section 1, "The idea"), with a
+ * hysteresis threshold whose published default is 3.0, twice the first
+ * setting (section 3, "Where the time goes"); every expert is fingerprinted
+ * at boot and every moved expert, plus a sample, again after swapping,
+ * wherever it now lives (section 4, the table of checks).  A manager tick is:
+ * moe_count_picks after each layer's routing (on the device, capturable),
+ * then between steps a host copy of the counts, moe_residency_plan (host),
+ * and moe_residency_swap (device).  Outputs do not depend on where experts
+ * live, so a swap never changes a layer's results.
+ * ------------------------------------------------------------------------- */
+
+/* Most swaps one moe_residency_swap / moe_residency_plan call handles. */
+#define MOE_MAX_SWAPS 64
+
+/* counts[e] += number of (token, pick) pairs of topk_ids [T][k] routed to e
+ * (ids outside [0,E) not counted); with clear != 0 counts is zeroed first
+ * (by a kernel, so the call may be captured in a graph).  counts: device
+ * int32 [E].  T = 0 with clear only zeroes. */
+moe_status moe_count_picks(const moe_shape *s, int32_t n_tokens, const int32_t *topk_ids, int32_t *counts,
+                           int32_t clear, void *stream);
+
+/* Host-side swap rule of one layer (no GPU work; all pointers are host memory).
+ *   score[e] <- decay * score[e] + counts_host[e]  (float64; the product is
+ *   rounded, then the sum); then cold experts in decreasing score against hot
+ *   experts in increasing score (equal scores: lower expert index first): the
+ *   i-th cold expert replaces the i-th hot one while
+ *   score_cold > threshold * max(score_hot, min_score), at most max_swaps times.
+ * Writes the pairs as pairs_out[2i] = cold expert promoted, pairs_out[2i+1] =
+ * hot expert demoted (room for 2*max_swaps int32), their number to
+ * *n_pairs_out, and applies them to slot_host (the promoted expert takes the
+ * demoted one's HBM index, the demoted one the promoted one's cold slot).
+ * slot_host must pass moe_residency_check; score entries must be finite and
+ * >= 0, counts >= 0, decay in [0,1], threshold > 0, min_score >= 0,
+ * 0 <= max_swaps <= MOE_MAX_SWAPS.  On error nothing is modified except
+ * *n_pairs_out = 0. */
+moe_status moe_residency_plan(const moe_shape *s, int32_t *slot_host, int32_t n_hot, int32_t n_cold,
+                              double *score, const int32_t *counts_host, double decay, double threshold,
+                              double min_score, int32_t max_swaps, int32_t *pairs_out, int32_t *n_pairs_out);
+
+/* Moves the experts of n_pairs (cold expert c, hot expert h) pairs, host array
+ * pairs[2*n_pairs] as written by moe_residency_plan: c's bytes from its host
+ * slot to h's HBM slot and h's bytes from HBM to c's host slot, then the
+ * device table r->slot is updated as moe_residency_plan updated its host
+ * copy.  The call WRITES r->slot, r->hot_base and r->host_cold (the pointers
+ * are const only for the layer entry points) and uses c's scratch slot as
+ * staging, so it must be ordered after any layer that still reads these
+ * (same stream) and before the next layer that uses this layer's table.  A
+ * pair that the device table does not show as (cold, hot) is left alone.
+ * Errors: experts outside [0,E), an expert named twice, n_pairs outside
+ * [0, MOE_MAX_SWAPS], a residency with no hot or no cold experts, or direct
+ * read (no staging) -> nothing enqueued. */
+moe_status moe_residency_swap(const moe_shape *s, const moe_residency *r, const int32_t *pairs, int32_t n_pairs,
+                              void *stream);
+
+/* Byte audit: out[p] (device uint64 [n]) = fingerprint of expert experts[p]
+ * (device int32 [n]) at its home: hot_base + slot*B when hot, host_cold +
+ * c*B when cold (the pinned pool, not the scratch copy).  Fingerprint: the
+ * sum modulo 2^64 over the blob's little-endian 64-bit words w_i of
+ * SplitMix64's output function (Steele, Lea and Flood 2014) applied to
+ * w_i + (i+1) * 0x9E3779B97F4A7C15.  An id outside [0,E) or an unusable table
+ * entry gives 0. */
+moe_status moe_fingerprint(const moe_shape *s, const moe_residency *r, const int32_t *experts, int32_t n,
+                           uint64_t *out, void *stream);
+
 /* Per-kernel timing, a tracing aid (off by default).  While enabled, each
  * kernel the library enqueues carries a start/stop HIP event pair stamped by
  * its own dispatch, so the times are kernel execution times.

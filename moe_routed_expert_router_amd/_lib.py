@@ -19,6 +19,7 @@ EXPORTS = (
     "moe_status_string", "moe_last_error", "moe_shape_check", "moe_expert_bytes",
     "moe_workspace_bytes", "moe_residency_check", "moe_host_alloc", "moe_host_free",
     "moe_route", "moe_pick_set", "moe_gather_cold", "moe_expert_ffn", "moe_layer_forward",
+    "moe_count_picks", "moe_residency_plan", "moe_residency_swap", "moe_fingerprint",
     "moe_profile_enable", "moe_profile_reset", "moe_profile_read",
 )
 
@@ -77,6 +78,11 @@ def _load():
                                      P, P, c_size_t, P]),
         "moe_layer_forward": (c_int32, [POINTER(MoeShape), c_int32, P, P, P, c_int32,
                                         POINTER(MoeResidency), P, P, c_int32, P, P, c_size_t, P]),
+        "moe_count_picks": (c_int32, [POINTER(MoeShape), c_int32, P, P, c_int32, P]),
+        "moe_residency_plan": (c_int32, [POINTER(MoeShape), P, c_int32, c_int32, P, P, ctypes.c_double,
+                                         ctypes.c_double, ctypes.c_double, c_int32, P, POINTER(c_int32)]),
+        "moe_residency_swap": (c_int32, [POINTER(MoeShape), POINTER(MoeResidency), P, c_int32, P]),
+        "moe_fingerprint": (c_int32, [POINTER(MoeShape), POINTER(MoeResidency), P, c_int32, P, P]),
         "moe_profile_enable": (c_int32, [c_int32]),
         "moe_profile_reset": (c_int32, []),
         "moe_profile_read": (c_int32, [c_int32, POINTER(c_char_p), POINTER(ctypes.c_int64),
@@ -206,6 +212,45 @@ def moe_layer_forward(s: MoeShape, x, w_router, bias, renormalize: bool, r: MoeR
     _check(lib.moe_layer_forward(ctypes.byref(s), T, _ptr(x), _ptr(w_router), _ptr(bias), int(bool(renormalize)),
                                  ctypes.byref(r), _ptr(topk_ids), _ptr(topk_w), _out_dtype(out), _ptr(out),
                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+MOE_MAX_SWAPS = 64
+
+
+def moe_count_picks(s: MoeShape, topk_ids, counts, clear: bool = False, stream=None) -> None:
+    T = topk_ids.shape[0] if topk_ids is not None else 0
+    _check(lib.moe_count_picks(ctypes.byref(s), T, _ptr(topk_ids), _ptr(counts), int(bool(clear)),
+                               _stream(stream)))
+
+
+def moe_residency_plan(s: MoeShape, slot_host, n_hot: int, n_cold: int, score, counts_host, decay: float,
+                       threshold: float, min_score: float, max_swaps: int):
+    """Host-only.  slot_host (int32) and score (float64) are numpy arrays
+    updated in place; returns the pairs as an int32 array [n][2]."""
+    import numpy as np
+    for name, a, dt in (("slot_host", slot_host, np.int32), ("score", score, np.float64)):
+        if not (isinstance(a, np.ndarray) and a.dtype == dt and a.flags.c_contiguous):
+            raise TypeError(f"{name} must be a C-contiguous numpy {np.dtype(dt).name} array (updated in place)")
+    counts = np.ascontiguousarray(counts_host, dtype=np.int32)
+    pairs = np.zeros((max(max_swaps, 1), 2), dtype=np.int32)
+    n = c_int32()
+    _check(lib.moe_residency_plan(ctypes.byref(s), slot_host.ctypes.data, n_hot, n_cold, score.ctypes.data,
+                                  counts.ctypes.data, decay, threshold, min_score, max_swaps, pairs.ctypes.data,
+                                  ctypes.byref(n)))
+    return pairs[:n.value].copy()
+
+
+def moe_residency_swap(s: MoeShape, r: MoeResidency, pairs, stream=None) -> None:
+    """pairs: host int32 [n][2] (cold expert, hot expert)."""
+    import numpy as np
+    a = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
+    _check(lib.moe_residency_swap(ctypes.byref(s), ctypes.byref(r), a.ctypes.data if a.size else None,
+                                  a.shape[0], _stream(stream)))
+
+
+def moe_fingerprint(s: MoeShape, r: MoeResidency, experts, out, stream=None) -> None:
+    _check(lib.moe_fingerprint(ctypes.byref(s), ctypes.byref(r), _ptr(experts), experts.numel(), _ptr(out),
+                               _stream(stream)))
 
 
 def moe_profile_enable(on: bool) -> None:

@@ -9,6 +9,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <cmath>
 #include <mutex>
 
 #include "kernels.hpp"
@@ -455,6 +456,93 @@ moe_status moe_layer_forward(const moe_shape *s, int32_t T, const uint16_t *x, c
         TRY(hip_status(moe::launch_gather(r->host_cold, r->scratch, g.blob_bytes, r->slot, w, L, st),
                        "gather launch"));
     TRY(enqueue_ffn(s, T, x, topk_ids, topk_w, out_dtype, out, w, L, st));
+    return ok();
+}
+
+moe_status moe_count_picks(const moe_shape *s, int32_t T, const int32_t *topk_ids, int32_t *counts, int32_t clear,
+                           void *stream) {
+    TRY(check_shape(s));
+    TRY(check_tokens(T));
+    const int E = s->n_experts, k = s->top_k;
+    TRY(check_ptr(counts, (size_t)E * 4, 4, "counts"));
+    if (T > 0) TRY(check_ptr(topk_ids, (size_t)T * k * 4, 4, "topk_ids"));
+    if (T == 0 && !clear) return ok();
+    TRY(hip_status(moe::launch_count_picks(topk_ids, T * k, E, counts, clear != 0, static_cast<hipStream_t>(stream)),
+                   "pick count launch"));
+    return ok();
+}
+
+moe_status moe_residency_plan(const moe_shape *s, int32_t *slot_host, int32_t n_hot, int32_t n_cold, double *score,
+                              const int32_t *counts_host, double decay, double threshold, double min_score,
+                              int32_t max_swaps, int32_t *pairs_out, int32_t *n_pairs_out) {
+    TRY(check_shape(s));
+    if (!score || !counts_host || !pairs_out || !n_pairs_out)
+        return fail(MOE_ERR_INVALID_ARG, "score, counts_host, pairs_out and n_pairs_out must not be NULL");
+    *n_pairs_out = 0;
+    TRY(moe_residency_check(s, slot_host, n_hot, n_cold));
+    if (!(decay >= 0.0 && decay <= 1.0)) return fail(MOE_ERR_INVALID_ARG, "decay %g outside [0, 1]", decay);
+    if (!(threshold > 0.0) || !std::isfinite(threshold))
+        return fail(MOE_ERR_INVALID_ARG, "threshold %g must be positive and finite", threshold);
+    if (!(min_score >= 0.0) || !std::isfinite(min_score))
+        return fail(MOE_ERR_INVALID_ARG, "min_score %g must be >= 0 and finite", min_score);
+    if (max_swaps < 0 || max_swaps > MOE_MAX_SWAPS)
+        return fail(MOE_ERR_INVALID_ARG, "max_swaps %d outside [0, %d]", max_swaps, MOE_MAX_SWAPS);
+    const int E = s->n_experts;
+    for (int e = 0; e < E; ++e) {
+        if (!(score[e] >= 0.0) || !std::isfinite(score[e]))
+            return fail(MOE_ERR_INVALID_ARG, "score[%d] = %g must be >= 0 and finite", e, score[e]);
+        if (counts_host[e] < 0) return fail(MOE_ERR_INVALID_ARG, "counts_host[%d] = %d is negative", e, counts_host[e]);
+    }
+    *n_pairs_out = moe::plan_swaps(E, slot_host, score, counts_host, decay, threshold, min_score, max_swaps, pairs_out);
+    return ok();
+}
+
+moe_status moe_residency_swap(const moe_shape *s, const moe_residency *r, const int32_t *pairs, int32_t n_pairs,
+                              void *stream) {
+    TRY(check_shape(s));
+    if (n_pairs < 0 || n_pairs > MOE_MAX_SWAPS)
+        return fail(MOE_ERR_INVALID_ARG, "n_pairs %d outside [0, %d]", n_pairs, MOE_MAX_SWAPS);
+    TRY(check_residency(s, r));
+    if (n_pairs == 0) return ok();
+    if (!pairs) return fail(MOE_ERR_INVALID_ARG, "pairs is NULL");
+    if (r->n_hot == 0 || r->n_cold == 0) return fail(MOE_ERR_BAD_RESIDENCY, "a swap needs hot and cold experts");
+    if (direct_read(r))
+        return fail(MOE_ERR_BAD_RESIDENCY, "direct read (scratch == host_cold) has no staging area for a swap");
+    const int E = s->n_experts;
+    static thread_local unsigned char used[moe::kMaxExperts];
+    memset(used, 0, sizeof(used));
+    moe::SwapList l{};
+    l.n = n_pairs;
+    for (int p = 0; p < n_pairs; ++p) {
+        const int32_t c = pairs[2 * p], h = pairs[2 * p + 1];
+        if (c < 0 || c >= E || h < 0 || h >= E)
+            return fail(MOE_ERR_INVALID_ARG, "pair %d: expert outside [0, %d)", p, E);
+        if (used[c] || used[h] || c == h)
+            return fail(MOE_ERR_INVALID_ARG, "pair %d: expert %d or %d appears twice in the list", p, c, h);
+        used[c] = used[h] = 1;
+        l.cold[p] = c;
+        l.hot[p] = h;
+    }
+    const size_t B = moe::BlobLayout::make(s->hidden, s->inter).bytes;
+    TRY(hip_status(moe::launch_residency_swap(const_cast<int32_t *>(r->slot), const_cast<uint8_t *>(r->hot_base),
+                                              const_cast<uint8_t *>(r->host_cold), r->scratch, B, E, r->n_hot,
+                                              r->n_cold, l, static_cast<hipStream_t>(stream)),
+                   "residency swap launch"));
+    return ok();
+}
+
+moe_status moe_fingerprint(const moe_shape *s, const moe_residency *r, const int32_t *experts, int32_t n,
+                           uint64_t *out, void *stream) {
+    TRY(check_shape(s));
+    if (n < 0 || n > (1 << 20)) return fail(MOE_ERR_INVALID_ARG, "n %d outside [0, 2^20]", n);
+    TRY(check_residency(s, r));
+    if (n == 0) return ok();
+    TRY(check_ptr(experts, (size_t)n * 4, 4, "experts"));
+    TRY(check_ptr(out, (size_t)n * 8, 8, "out"));
+    const size_t B = moe::BlobLayout::make(s->hidden, s->inter).bytes;
+    TRY(hip_status(moe::launch_fingerprint(experts, n, r->slot, r->hot_base, r->host_cold, B, s->n_experts, r->n_hot,
+                                           r->n_cold, out, static_cast<hipStream_t>(stream)),
+                   "fingerprint launch"));
     return ok();
 }
 

@@ -105,4 +105,30 @@ hipError_t launch_ffn_gemm(const FfnArgs &a, const GroupView &gv, int max_tiles,
 // Largest T routed by the single-block select-and-group kernel.
 constexpr int kSmallRouteTokens = 32;
 
+// Adaptive residency (residency.hip).
+// counts[E] (+)= pairs per expert; ids outside [0,E) ignored; clear zeroes
+// counts first with a fill kernel.
+hipError_t launch_count_picks(const int32_t *ids, int n_pairs, int E, int32_t *counts, bool clear, hipStream_t st);
+
+// Swaps of (cold expert, hot expert) pairs, passed by value to the kernels.
+constexpr int kMaxSwaps = 64;
+struct SwapList {
+    int32_t n;
+    int32_t cold[kMaxSwaps];
+    int32_t hot[kMaxSwaps];
+};
+hipError_t launch_residency_swap(int32_t *slot, uint8_t *hot_base, uint8_t *host_cold, uint8_t *scratch,
+                                 size_t blob_bytes, int E, int n_hot, int n_cold, const SwapList &l,
+                                 hipStream_t st);
+
+// out[p] = fingerprint of expert experts[p] at its home (HBM pool or host pool).
+hipError_t launch_fingerprint(const int32_t *experts, int n, const int32_t *slot, const uint8_t *hot_base,
+                              const uint8_t *host_cold, size_t blob_bytes, int E, int n_hot, int n_cold,
+                              uint64_t *out, hipStream_t st);
+
+// Host side of the manager: decayed scores and the swap rule; returns the
+// number of pairs written to pairs[2*i], pairs[2*i+1] and updates slot and score.
+int plan_swaps(int E, int32_t *slot, double *score, const int32_t *counts, double decay, double threshold,
+               double min_score, int max_swaps, int32_t *pairs);
+
 }  // namespace moe

@@ -108,3 +108,80 @@ def test_null_arguments_rejected_before_any_launch():
     assert st == moe.MOE_ERR_BAD_RESIDENCY
     with pytest.raises(moe.MoeError):
         moe.moe_host_free(0)
+
+
+# ------------------------- adaptive residency (host) -------------------------
+def _random_table(rng, E, n_hot):
+    hot = set(rng.choice(E, n_hot, replace=False).tolist())
+    slot = np.empty(E, dtype=np.int32)
+    h = c = 0
+    for e in range(E):
+        if e in hot:
+            slot[e], h = h, h + 1
+        else:
+            slot[e], c = -c - 1, c + 1
+    return slot
+
+
+def test_residency_plan_matches_oracle(rng):
+    """The library's swap rule (host C++) against oracle.residency, bit for
+    bit: pairs, the updated table and the float64 scores, over many ticks."""
+    from oracle import residency as ores
+    for E, n_hot in ((8, 5), (64, 40), (384, 255)):
+        s = moe.shape(256, 128, E, 2)
+        for threshold, decay, min_score, max_swaps in ((3.0, 0.9, 1.0, 8), (1.5, 0.5, 0.5, 64), (1.0, 1.0, 0.0, 3)):
+            slot = _random_table(rng, E, n_hot)
+            score = np.zeros(E)
+            o_slot, o_score = slot.copy(), score.copy()
+            for tick in range(12):
+                # drifting skewed counts, with ties (integers) and quiet experts
+                w = rng.permutation(E)[: max(1, E // 3)]
+                counts = np.zeros(E, dtype=np.int32)
+                counts[w] = rng.integers(0, 6, w.size)
+                pairs = moe.moe_residency_plan(s, slot, n_hot, E - n_hot, score, counts, decay, threshold,
+                                               min_score, max_swaps)
+                o_pairs, o_slot, o_score = ores.manager_tick(o_slot, o_score, counts, decay, threshold, min_score,
+                                                             max_swaps)
+                assert [tuple(p) for p in pairs.tolist()] == o_pairs, (E, tick)
+                assert np.array_equal(slot, o_slot)
+                assert np.array_equal(score.view(np.uint64), o_score.view(np.uint64))
+                moe.moe_residency_check(s, slot, n_hot, E - n_hot)
+
+
+def test_residency_plan_rejects_bad_input():
+    s = moe.shape(256, 128, 8, 2)
+    slot = np.array([0, 1, 2, 3, 4, -1, -2, -3], dtype=np.int32)
+    ok = dict(decay=0.5, threshold=3.0, min_score=1.0, max_swaps=4)
+    cases = [
+        (dict(ok, decay=1.5), "decay"), (dict(ok, threshold=0.0), "threshold"),
+        (dict(ok, min_score=-1.0), "min_score"), (dict(ok, max_swaps=moe.MOE_MAX_SWAPS + 1), "max_swaps"),
+    ]
+    for kw, what in cases:
+        score = np.zeros(8)
+        before = slot.copy()
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_residency_plan(s, slot, 5, 3, score, np.zeros(8, np.int32), **kw)
+        assert ei.value.status == moe.MOE_ERR_INVALID_ARG and what in moe.moe_last_error()
+        assert np.array_equal(slot, before)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_residency_plan(s, slot, 5, 3, np.full(8, np.nan), np.zeros(8, np.int32), **ok)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_residency_plan(s, np.array([0, 0, 2, 3, 4, -1, -2, -3], np.int32), 5, 3, np.zeros(8),
+                               np.zeros(8, np.int32), **ok)
+    assert ei.value.status == moe.MOE_ERR_BAD_RESIDENCY
+
+
+def test_residency_device_calls_validate_first():
+    lib = moe.lib
+    s = moe.shape(256, 128, 8, 2)
+    r = moe.residency(None, None, None, None, 5, 3)
+    pairs = (ctypes.c_int32 * 4)(5, 0, 6, 1)
+    assert lib.moe_residency_swap(ctypes.byref(s), ctypes.byref(r), pairs, 65, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_residency_swap(ctypes.byref(s), ctypes.byref(r), pairs, 2, None) == moe.MOE_ERR_INVALID_ARG
+    assert "NULL" in moe.moe_last_error()
+    bad = moe.residency(None, None, None, None, 5, 4)
+    assert lib.moe_residency_swap(ctypes.byref(s), ctypes.byref(bad), pairs, 2, None) == moe.MOE_ERR_BAD_RESIDENCY
+    assert lib.moe_fingerprint(ctypes.byref(s), ctypes.byref(r), None, -1, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_count_picks(ctypes.byref(s), 4, None, None, 0, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_count_picks(ctypes.byref(s), -1, None, None, 0, None) == moe.MOE_ERR_UNSUPPORTED_SHAPE
