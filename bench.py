@@ -429,6 +429,167 @@ def _verify_point(wl, cal, rho, pools, S, reps):
         torch.cuda.empty_cache()
 
 
+def measure_adaptive(layers: int = 8, warm: int = 1500, steps: int = 1000, drift: float = 0.2,
+                     decay: float = 0.999, min_score: float = 1.0, max_swaps: int = 4,
+                     thresholds=(None, 1.5, 3.0), pool: int = 1024, drift_every: int | None = None) -> dict:
+    """Adaptive residency on drifting traffic: `layers` hot/cold decode layers
+    (255 resident / 129 in pinned host memory, one stream, one token per
+    step) whose traffic has drifted from the calibration the hot sets were
+    chosen on (one round of drift over `drift` of the Zipf ranks).  Per mode
+    (static map, or the manager with each hysteresis threshold): `warm`
+    steps to adapt, then `steps` measured.  A step is the layers' forwards
+    and pick counts replayed from one HIP graph; the manager reads the
+    counts, plans on the host and enqueues the swaps between steps.  Reports
+    forward and swap time per step, cold experts gathered and swaps per
+    1000 steps, and a final byte audit of every expert against its boot
+    fingerprint.  drift_every: the traffic keeps drifting, one more round
+    every that many steps (mixed traffic that never settles)."""
+    import torch
+    import moe_routed_expert_router_amd as moe
+    from synth import gen
+    from tests.gpu_setup import Layer
+    wl = gen.workload("hotcold8")
+    cal = gen.load_calibration()
+    E, H = wl.n_experts, wl.hidden
+    Ls = []
+    try:
+        for l in range(layers):
+            L = Layer(wl, layer=l, T=1, cal=cal)
+            b = gen.drifted_zipf_prior(wl.seed, l, E, cal["alpha"], drift, 1)
+            L.bias_np = b
+            L.bias.copy_(torch.from_numpy(b))
+            Ls.append(L)
+        base_hot = [set(L.hot) for L in Ls]
+        n_rounds = 1 + (0 if not drift_every else (warm + steps - 1) // drift_every)
+        priors = [[torch.from_numpy(gen.drifted_zipf_prior(wl.seed, l, E, cal["alpha"], drift, r + 1)).cuda()
+                   for r in range(n_rounds)] for l in range(layers)]
+        toks = [torch.from_numpy(gen.tokens_bf16(wl.seed + 7, l, pool, H).view(np.int16)).cuda()
+                for l in range(layers)]
+        xbuf = [torch.empty((1, H), dtype=torch.int16, device="cuda") for _ in range(layers)]
+        counts = torch.zeros((layers, E), dtype=torch.int32, device="cuda")
+        all_e = torch.arange(E, dtype=torch.int32, device="cuda")
+        fps = torch.empty((layers, E), dtype=torch.int64, device="cuda")
+
+        def fingerprint_all():
+            for l, L in enumerate(Ls):
+                moe.moe_fingerprint(L.shape, L.residency, all_e, fps[l])
+            torch.cuda.synchronize()
+            return fps.cpu().numpy().copy()
+
+        boot = fingerprint_all()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        for l, L in enumerate(Ls):
+            L.x = xbuf[l]
+            xbuf[l].copy_(toks[l][0:1])
+
+        def body():
+            for l, L in enumerate(Ls):
+                L.forward(stream=s.cuda_stream)
+                moe.moe_count_picks(L.shape, L.ids, counts[l], clear=True, stream=s.cuda_stream)
+
+        with torch.cuda.stream(s):
+            body()
+        s.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s, capture_error_mode="relaxed"):
+            body()
+        torch.cuda.synchronize()
+
+        def restore_map():
+            # move the hot sets back to the calibrated ones (which slot holds
+            # which expert does not matter)
+            for l, L in enumerate(Ls):
+                back_in = [e for e in base_hot[l] if L.slot_np[e] < 0]
+                back_out = [e for e in range(E) if L.slot_np[e] >= 0 and e not in base_hot[l]]
+                pairs = list(zip(back_in, back_out))
+                for i in range(0, len(pairs), moe.MOE_MAX_SWAPS):
+                    chunk = pairs[i:i + moe.MOE_MAX_SWAPS]
+                    moe.moe_residency_swap(L.shape, L.residency, chunk)
+                    for c, h in chunk:
+                        L.slot_np[c], L.slot_np[h] = L.slot_np[h], L.slot_np[c]
+            torch.cuda.synchronize()
+            for L in Ls:
+                assert np.array_equal(L.slot.cpu().numpy(), L.slot_np)
+
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        out = {}
+        for th in thresholds:
+            name = "static" if th is None else f"adaptive_threshold{th:g}"
+            restore_map()
+            scores = [np.zeros(E) for _ in Ls]
+            fwd_ms = swap_ms = 0.0
+            cold_picks = swaps = 0
+            t_host = 0.0
+            for i in range(warm + steps):
+                if i == 0 or (drift_every and i % drift_every == 0):
+                    r = 0 if not drift_every else i // drift_every
+                    for l, L in enumerate(Ls):
+                        L.bias.copy_(priors[l][r])
+                for l in range(layers):
+                    xbuf[l].copy_(toks[l][i % pool:i % pool + 1])
+                ev[0].record()
+                graph.replay()                    # on the current stream, as everything below
+                ev[1].record()
+                c = counts.cpu().numpy()          # waits for the step
+                measured = i >= warm
+                if measured:
+                    fwd_ms += ev[0].elapsed_time(ev[1])
+                    cold_picks += sum(int(np.sum((c[l] > 0) & (L.slot_np < 0))) for l, L in enumerate(Ls))
+                if th is None:
+                    continue
+                th0 = time.perf_counter()
+                plans = [moe.moe_residency_plan(L.shape, L.slot_np, L.n_hot, L.n_cold, scores[l], c[l], decay,
+                                                th, min_score, max_swaps) for l, L in enumerate(Ls)]
+                t1 = time.perf_counter()
+                n = sum(len(p) for p in plans)
+                if n:
+                    ev[2].record()
+                    for L, p in zip(Ls, plans):
+                        if len(p):
+                            moe.moe_residency_swap(L.shape, L.residency, p)
+                    ev[3].record()
+                    if measured:
+                        ev[3].synchronize()
+                        swap_ms += ev[2].elapsed_time(ev[3])
+                if measured:
+                    swaps += n
+                    t_host += t1 - th0
+            torch.cuda.synchronize()
+            B = Ls[0].B
+            entry = {"forward_ms_per_step": round(fwd_ms / steps, 4),
+                     "swap_ms_per_step": round(swap_ms / steps, 4),
+                     "ms_per_step": round((fwd_ms + swap_ms) / steps, 4),
+                     "tokens_per_s": round(steps / ((fwd_ms + swap_ms) * 1e-3), 1),
+                     "cold_experts_per_step": round(cold_picks / steps, 3),
+                     "gathered_MB_per_step": round(cold_picks * B / steps / 1e6, 2),
+                     "swaps_per_1000_steps": round(1000 * swaps / steps, 1),
+                     "moved_MB_per_step": round(2 * swaps * B / steps / 1e6, 2),
+                     "plan_us_per_step": round(1e6 * t_host / steps, 1)}
+            out[name] = entry
+            log(f"[bench] residency {name}: forward {entry['forward_ms_per_step']:.3f} ms + swaps "
+                f"{entry['swap_ms_per_step']:.3f} ms per step ({layers} layers, 1 token), "
+                f"{entry['cold_experts_per_step']:.2f} cold experts/step, {entry['swaps_per_1000_steps']:.0f} "
+                f"swaps per 1000 steps")
+        after = fingerprint_all()
+        mism = 0
+        for l, L in enumerate(Ls):
+            mism += int(np.sum(after[l] != boot[l]))
+        out["audit"] = {"experts_checked": int(layers * E), "mismatches": mism}
+        out["setup"] = {"layers": layers, "tokens_per_step": 1, "warm_steps": warm, "measured_steps": steps,
+                        "drift_fraction": drift, "drift_every_steps": drift_every, "decay": decay,
+                        "min_score": min_score,
+                        "max_swaps_per_layer_tick": max_swaps}
+        log(f"[bench] residency audit: {mism} mismatches over {layers * E} experts")
+        del graph
+        return out
+    finally:
+        for L in Ls:
+            L.close()
+        del Ls
+        torch.cuda.empty_cache()
+
+
 def measure_direct_read(batches=(1, 8, 32), layers: int = 4, reps: int = 8) -> dict:
     """Gather-then-compute against direct read (the FFN reads the picked cold
     experts in place from pinned host memory) for hot/cold decode layers
@@ -616,6 +777,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batch8", action="store_true", help="skip the batch-8 hot/cold secondary figures")
+    ap.add_argument("--primary-only", action="store_true", help="skip every secondary figure")
+    ap.add_argument("--no-adaptive", action="store_true", help="skip the adaptive-residency secondary figures")
     ap.add_argument("--no-verify", action="store_true", help="skip the speculative-verify secondary figures")
     ap.add_argument("--no-layer-copy", action="store_true",
                     help="skip the whole-layer cold copy baseline")
@@ -628,6 +791,10 @@ def main():
                     help="first run one plain float64 copy of this many MiB (a known-size kernel for "
                          "scaling hardware byte counters)")
     a = ap.parse_args()
+    if a.primary_only:
+        for k in ("no_batch8", "no_adaptive", "no_verify", "no_layer_copy", "no_direct_read", "no_ffn_batches",
+                  "no_step40"):
+            setattr(a, k, True)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
@@ -720,6 +887,11 @@ def main():
     if not a.no_direct_read and a.workload == "decode1":
         log("[bench] secondary: gather-then-compute vs direct read of cold experts (batch 1/8/32)")
         extra["direct_read"] = measure_direct_read()
+
+    if not a.no_adaptive and a.workload == "decode1":
+        log("[bench] secondary: adaptive residency on drifting traffic")
+        extra["adaptive_residency"] = {"drifted_once": measure_adaptive(),
+                                       "drifting": measure_adaptive(drift_every=250)}
 
     if not a.no_verify and a.workload == "decode1":
         log("[bench] secondary: speculative-verify steps (streams x (1 + draft), correlated windows)")

@@ -41,7 +41,7 @@ __all__ = [
     "fill_expert_blobs_device", "tokens_bf16", "router_weight", "zipf_prior",
     "load_calibration", "hot_set", "residency_slots", "bf16_round_bits",
     "CALIBRATION_PATH", "verify_window", "verify_tokens_bf16", "load_verify_calibration",
-    "VERIFY_CALIBRATION_PATH",
+    "VERIFY_CALIBRATION_PATH", "drifted_zipf_prior",
 ]
 
 M32 = 0xFFFFFFFF
@@ -50,6 +50,7 @@ M32 = 0xFFFFFFFF
 TAG_W13_NIB, TAG_W13_SCALE, TAG_W2_NIB, TAG_W2_SCALE = 1, 2, 3, 4
 TAG_TOKENS, TAG_ROUTER, TAG_ZIPF_RANK = 5, 6, 7
 TAG_VERIFY_SHARED, TAG_VERIFY_OWN = 8, 9
+TAG_DRIFT = 10
 
 SCALE_LO, SCALE_N = 123, 5          # e8m0 bytes uniform over 123..127 (2^-4..2^0)
 
@@ -297,6 +298,23 @@ def verify_tokens_bf16(seed: int, layer: int, streams: int, window: int, H: int,
     n = _philox(seed, TAG_VERIFY_OWN, layer).standard_normal((streams, window, H), dtype=np.float32)
     x = np.float32(math.sqrt(rho)) * a[:, None, :] + np.float32(math.sqrt(1.0 - rho)) * n
     return bf16_round_bits(x.reshape(streams * window, H))
+
+
+def drifted_zipf_prior(seed: int, layer: int, E: int, alpha: float, frac: float, rounds: int,
+                       s: float = 1.1) -> np.ndarray:
+    """zipf_prior after `rounds` rounds of drift: each round takes round(frac*E)
+    random positions of the rank permutation and shuffles their ranks among
+    themselves (traffic whose favourite experts differ from the calibration's;
+    rounds = 0 is zipf_prior itself)."""
+    g = _philox(seed, TAG_ZIPF_RANK, layer)
+    rank = g.permutation(E).astype(np.float64) + 1.0
+    m = int(round(frac * E))
+    for r in range(rounds):
+        k1, k2 = stream_keys(seed, TAG_DRIFT, layer, r)
+        d = np.random.Generator(np.random.Philox(key=(k1 << 32) | k2))
+        pos = d.choice(E, m, replace=False)
+        rank[pos] = rank[d.permutation(pos)]
+    return (-alpha * s * np.log(rank)).astype(np.float32)
 
 
 # ----------------------------- calibration data -----------------------------

@@ -1,4 +1,5 @@
-"""The speculative-verify input recipe: the draft schedule, the window
+"""Input recipes: the drifted Zipf prior, and the speculative-verify
+recipe: the draft schedule, the window
 correlation of the generated tokens, and the distinct-expert multiplier the
 calibration fitted (3.7x one token's experts for a 1 + 5 window, the GB300
 inference write-up, speculative-fetching row of its table of what was
@@ -49,3 +50,18 @@ def test_calibrated_multiplier_on_fresh_tokens():
         z0 = router_logits(x0, gen.router_weight(0, layer, E, H), gen.zipf_prior(0, layer, E, zipf["alpha"]))
         ids0 = select_topk(z0, K).reshape(n, W * K)
         assert np.mean([len(np.unique(r)) for r in ids0]) / K > mult + 0.3
+
+
+def test_drifted_prior():
+    """Drift keeps the prior's values (a permutation of the same ranks) and
+    moves about frac of them per round; zero rounds is the calibrated prior."""
+    alpha = gen.load_calibration()["alpha"]
+    base = gen.zipf_prior(0, 3, 384, alpha)
+    assert np.array_equal(gen.drifted_zipf_prior(0, 3, 384, alpha, 0.3, 0), base)
+    d1 = gen.drifted_zipf_prior(0, 3, 384, alpha, 0.3, 1)
+    d2 = gen.drifted_zipf_prior(0, 3, 384, alpha, 0.3, 2)
+    assert np.array_equal(np.sort(d1), np.sort(base)) and np.array_equal(np.sort(d2), np.sort(base))
+    moved1 = int(np.sum(d1 != base))
+    assert 0.2 * 384 < moved1 <= 0.3 * 384 + 1
+    assert np.sum(d2 != base) > moved1
+    assert np.array_equal(gen.drifted_zipf_prior(0, 3, 384, alpha, 0.3, 1), d1)
