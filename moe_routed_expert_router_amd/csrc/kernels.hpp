@@ -107,7 +107,7 @@ constexpr int kSmallRouteTokens = 32;
 
 // Adaptive residency (residency.hip).
 // counts[E] (+)= pairs per expert; ids outside [0,E) ignored; clear zeroes
-// counts first with a fill kernel.
+// counts first (in the same kernel at decode sizes, else a fill kernel).
 hipError_t launch_count_picks(const int32_t *ids, int n_pairs, int E, int32_t *counts, bool clear, hipStream_t st);
 
 // Swaps of (cold expert, hot expert) pairs, passed by value to the kernels.

@@ -48,7 +48,31 @@ __global__ __launch_bounds__(kCountThreads) void count_picks(const int32_t *__re
         if (hist[e]) atomicAdd(&counts[e], hist[e]);
 }
 
+// Up to kCountOneBlock pairs (every decode step): one block counts them all
+// and writes (or adds) every bin itself, one launch and no global atomics.
+constexpr int kCountOneBlock = 8192;
+constexpr int kCountOneThreads = 1024;
+
+__global__ __launch_bounds__(kCountOneThreads) void count_picks_one(const int32_t *__restrict__ ids, int n_pairs,
+                                                                    int E, int32_t *__restrict__ counts,
+                                                                    int clear) {
+    __shared__ int32_t hist[kMaxExperts];
+    for (int e = threadIdx.x; e < E; e += kCountOneThreads) hist[e] = 0;
+    __syncthreads();
+    for (int p = threadIdx.x; p < n_pairs; p += kCountOneThreads) {
+        const int e = ids[p];
+        if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += kCountOneThreads) counts[e] = (clear ? 0 : counts[e]) + hist[e];
+}
+
 hipError_t launch_count_picks(const int32_t *ids, int n_pairs, int E, int32_t *counts, bool clear, hipStream_t st) {
+    if (n_pairs <= kCountOneBlock) {
+        MOE_LAUNCH("count_picks_one", count_picks_one, dim3(1), dim3(kCountOneThreads), 0, st, ids, n_pairs, E,
+                   counts, clear ? 1 : 0);
+        return hipGetLastError();
+    }
     if (clear) MOE_LAUNCH("fill_i32", fill_i32, dim3((E + kCountThreads - 1) / kCountThreads), dim3(kCountThreads),
                           0, st, counts, E, 0);
     if (n_pairs > 0) {
