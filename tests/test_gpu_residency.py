@@ -230,3 +230,59 @@ def test_swap_rejects_direct_read_and_bad_pairs():
         assert torch.equal(L.slot, before)
     finally:
         L.close()
+
+
+def test_swap_of_the_most_pairs_at_once():
+    """MOE_MAX_SWAPS pairs in one call (the grid's pair axis at its largest):
+    table, bytes (audited) and outputs as the oracle's moves say."""
+    wl = gen.workload("hotcold8")
+    L = Layer(wl, T=8)
+    try:
+        boot = fingerprints(L, range(L.E))
+        out0 = L.forward().clone()
+        n = moe.MOE_MAX_SWAPS
+        pairs = np.array(list(zip(L.cold[:n], L.hot[-n:])), dtype=np.int32)
+        want = L.slot_np.copy()
+        for c, h in pairs:
+            want[c], want[h] = want[h], want[c]
+        moe.moe_residency_swap(L.shape, L.residency, pairs)
+        torch.cuda.synchronize()
+        assert np.array_equal(L.slot.cpu().numpy(), want)
+        L.slot_np = want
+        assert fingerprints(L, range(L.E)) == boot
+        out1 = L.forward()
+        torch.cuda.synchronize()
+        assert torch.equal(out1, out0)
+    finally:
+        L.close()
+
+
+def test_fingerprint_past_the_grid_row_limit():
+    """More fingerprints than one launch's grid rows (65,535): every id,
+    repeated, gets its expert's value; out-of-range ids give 0."""
+    E = 8
+    s = moe.shape(256, 128, E, 2)
+    B = moe.moe_expert_bytes(s)
+    rng = np.random.default_rng(3)
+    blobs = rng.integers(0, 256, (E, B), dtype=np.uint8)
+    hot = torch.from_numpy(blobs[:6].copy()).cuda()
+    from tests.gpu_setup import HostBuffer
+    host = HostBuffer(2 * B)
+    try:
+        host.np[:] = blobs[6:].reshape(-1)
+        scratch = torch.empty((2, B), dtype=torch.uint8, device="cuda")
+        slot = torch.tensor([0, 1, 2, 3, 4, 5, -1, -2], dtype=torch.int32, device="cuda")
+        r = moe.residency(slot, hot, host.dev, scratch, 6, 2)
+        n = 70000
+        ids_np = rng.integers(-1, E + 1, n).astype(np.int32)
+        ids = torch.from_numpy(ids_np).cuda()
+        out = torch.empty(n, dtype=torch.int64, device="cuda")
+        moe.moe_fingerprint(s, r, ids, out)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().view(np.uint64)
+        ref = [ores.fingerprint(blobs[e]) for e in range(E)]
+        for i in range(n):
+            e = ids_np[i]
+            assert int(got[i]) == (ref[e] if 0 <= e < E else 0), i
+    finally:
+        host.close()
