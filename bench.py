@@ -41,19 +41,29 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash(kernel: str) -> str:
-    """Hash of the source file that defines `kernel` plus every shared header:
-    a counter summary stays valid while none of them changes."""
+def _code_only(text: str) -> str:
+    """C++ source without comments and with whitespace runs collapsed (string
+    literals are kept; the sources put no comment markers inside them)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def kernel_source_hash(kernel: str, csrc: str | None = None) -> str:
+    """Hash of the code (comments and layout ignored) of the source file that
+    defines `kernel` plus every shared header: a counter summary stays valid
+    while none of them changes."""
     import re
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "moe_routed_expert_router_amd", "csrc")
+    csrc = csrc or os.path.join(ROOT, "moe_routed_expert_router_amd", "csrc")
     files = sorted(os.listdir(csrc))
     pat = re.compile(r"__global__[^;{]*?\b" + re.escape(kernel) + r"\s*\(")
     for f in files:
-        text = open(os.path.join(csrc, f), "rb").read()
-        if f.endswith(".hpp") or (f.endswith(".hip") and pat.search(text.decode("utf-8", "replace"))):
+        text = open(os.path.join(csrc, f), "rb").read().decode("utf-8", "replace")
+        if f.endswith(".hpp") or (f.endswith(".hip") and pat.search(text)):
             h.update(f.encode())
-            h.update(text)
+            h.update(_code_only(text).encode())
     return h.hexdigest()[:16]
 
 
