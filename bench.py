@@ -701,9 +701,76 @@ def measure_layer_copy(T: int = 32, layers: int = 40, reps: int = 3) -> dict:
         torch.cuda.empty_cache()
 
 
-def measure_stack(name: str, steps: int, warmup: int, use_graph: bool) -> dict:
+def _stack_batch1(S, rows: int, steps: int) -> dict:
+    """One-stream decode steps on the same resident stack: one token per
+    layer, the token taken from row r of each layer's batch for step r (mod
+    rows), each row's 40-layer pass replayed from its own HIP graph; the
+    cold experts each step gathers are counted from the routing, and one
+    profiled eager pass over every row gives the gather's share of the
+    kernel time."""
+    import torch
+    import moe_routed_expert_router_amd as moe
+    full = [(L.x, L.ids, L.w, L.out) for L in S.layers]
+    ids_full = [L.ids.cpu().numpy() for L in S.layers]
+
+    def use_row(r):
+        for L, (x, ids, w, out) in zip(S.layers, full):
+            L.x, L.ids, L.w, L.out = x[r:r + 1], ids[r:r + 1], w[r:r + 1], out[r:r + 1]
+
+    graphs = []
+    try:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        for r in range(rows):
+            use_row(r)
+            S.forward()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s, capture_error_mode="relaxed"):
+                S.forward(stream=s)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            graphs[i % rows].replay()
+        torch.cuda.synchronize()
+        secs = time.perf_counter() - t0
+        moe.moe_profile_reset()
+        moe.moe_profile_enable(True)
+        for r in range(rows):
+            use_row(r)
+            S.forward()
+        torch.cuda.synchronize()
+        moe.moe_profile_enable(False)
+        stats = moe.moe_profile_read()
+        moe.moe_profile_reset()
+    finally:
+        del graphs
+        for L, (x, ids, w, out) in zip(S.layers, full):
+            L.x, L.ids, L.w, L.out = x, ids, w, out
+    total_ms = sum(ms for _, ms in stats.values())
+    gather_ms = stats.get("gather_cold", (0, 0.0))[1]
+    cold = [sum(1 for e in set(ids_full[l][r].tolist()) if L.slot_np[e] < 0) for r in range(rows)
+            for l, L in enumerate(S.layers)]
+    res = {"tokens_per_s": round(steps / secs, 1), "ms_per_step": round(1e3 * secs / steps, 4),
+           "token_rows_rotated": rows, "cold_experts_per_step": round(sum(cold) / rows, 2),
+           "gather_ms_per_step": round(gather_ms / rows, 4),
+           "gather_share_of_kernel_time": round(gather_ms / total_ms, 3) if total_ms else None}
+    log(f"[bench] one stream: {res['ms_per_step']:.3f} ms/step ({res['tokens_per_s']} tokens/s), "
+        f"{res['cold_experts_per_step']} cold experts gathered per step, gather "
+        f"{res['gather_ms_per_step']:.3f} ms/step")
+    return res
+
+
+def measure_stack(name: str, steps: int, warmup: int, use_graph: bool, one_token_rows: int = 0,
+                  steps_batch1: int = 64) -> dict:
     """Whole decode steps of a multi-layer workload (every layer in order on
-    one stream, one shared cold scratch); None if it does not fit the GPU."""
+    one stream, one shared cold scratch); None if it does not fit the GPU.
+    one_token_rows > 0 adds one-stream steps (one token per layer) on the
+    same stack."""
     import torch
     import moe_routed_expert_router_amd as moe
     from synth import gen
@@ -769,6 +836,8 @@ def measure_stack(name: str, steps: int, warmup: int, use_graph: bool) -> dict:
             entry["gather_link_GB_per_s"] = round(by["gather_cold"] / (role_us(prof, "gather_cold") * 1e-6) / 1e9, 2)
             entry["gather_bytes_per_layer"] = int(by["gather_cold"])
         log(f"[bench] {name}: {entry['ms_per_step']:.3f} ms/step, {entry['tokens_per_s']} tokens/s")
+        if one_token_rows:
+            entry["batch1"] = _stack_batch1(S, one_token_rows, steps_batch1)
         return entry
     finally:
         S.close()
@@ -917,7 +986,7 @@ def main():
 
     if not a.no_step40 and a.workload == "decode1":
         log("[bench] secondary: step40 (40 layers, batch 32, 255 hot / 129 cold, shared scratch)")
-        extra["step40_batch32"] = measure_stack("step40", 10, 2, not a.no_graph)
+        extra["step40_batch32"] = measure_stack("step40", 10, 2, not a.no_graph, one_token_rows=16)
         lc, st = extra.get("layer_copy"), extra["step40_batch32"]
         if lc and "tokens_per_s" in st:
             lc["picked_only_over_layer_copy"] = round(st["tokens_per_s"] / lc["tokens_per_s"], 1)
