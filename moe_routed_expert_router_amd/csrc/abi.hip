@@ -397,7 +397,7 @@ moe_status moe_layer_forward(const moe_shape *s, int32_t T, const uint16_t *x, c
     const moe::GroupArgs g = group_args(s, T, topk_ids, r);
     TRY(hip_status(moe::launch_route_logits(x, w_router, bias, T, H, E, z, st), "router logits launch"));
     const bool direct = direct_read(r);
-    if (T <= moe::kSmallRouteTokens && (r->n_cold == 0 || direct) && moe::ffn_select_fusable(T, k, H, s->inter)) {
+    if (T <= moe::kSmallRouteTokens && (r->n_cold == 0 || direct) && moe::ffn_select_fusable(T, k, E, H, s->inter)) {
         // no cold expert to gather: the gate/up kernel selects and groups by itself
         moe::FfnArgs a;
         a.x = x;
@@ -412,6 +412,40 @@ moe_status moe_layer_forward(const moe_shape *s, int32_t T, const uint16_t *x, c
         a.out = out;
         TRY(hip_status(moe::launch_ffn_select(a, z, renormalize != 0, topk_ids, topk_w, g, w, L, st),
                        "select + ffn launch"));
+        return ok();
+    }
+    if (T <= moe::kSmallRouteTokens && r->n_cold > 0 && !direct && moe::ffn_select_fusable(T, k, E, H, s->inter)) {
+        // decode with cold experts, no grouping launch: the gather (side
+        // stream) and the hot experts' gate/up (caller's stream) each take the
+        // top-k from the logits themselves; the cold experts' FFN and the
+        // combine follow the join, reading the pick set the gate/up published
+        moe::FfnArgs a;
+        a.x = x;
+        a.ids = topk_ids;
+        a.w = topk_w;
+        a.T = T;
+        a.H = H;
+        a.I = s->inter;
+        a.E = E;
+        a.k = k;
+        a.out_bf16 = out_dtype == MOE_OUT_BF16;
+        a.out = out;
+        const int P = T * k;
+        std::unique_lock<std::mutex> lock;
+        SideStream *side = nullptr;
+        TRY(side_stream(lock, &side));
+        TRY(hip_status(hipEventRecord(side->fork, st), "gather fork"));
+        TRY(hip_status(hipStreamWaitEvent(side->st, side->fork, 0), "gather fork"));
+        TRY(hip_status(moe::launch_gather_sel(z, T, E, k, r->slot, r->n_cold, r->host_cold, r->scratch, g.blob_bytes,
+                                              side->st),
+                       "gather launch"));
+        TRY(hip_status(hipEventRecord(side->join, side->st), "gather join"));
+        TRY(hip_status(moe::launch_ffn_select_hot(a, z, renormalize != 0, topk_ids, topk_w, g, w, L, st),
+                       "hot ffn launch"));
+        TRY(hip_status(hipStreamWaitEvent(st, side->join, 0), "gather join"));
+        lock.unlock();
+        TRY(hip_status(moe::launch_ffn_part(a, moe::kPartCold, r->n_cold < P ? r->n_cold : P, w, L, st),
+                       "cold ffn launch"));
         return ok();
     }
     if (T <= moe::kSmallRouteTokens) {

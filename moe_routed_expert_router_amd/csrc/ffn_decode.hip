@@ -235,8 +235,8 @@ __global__ __launch_bounds__(512) void ffn_gate_up_blk(const uint16_t *__restric
 // expert u.  grid (I/(16*RT), min(E, T*k)), 128 * RT * slices threads.
 template <int SPW, int NPL>
 __global__ __launch_bounds__(512) void ffn_gate_up_sel(const uint16_t *__restrict__ x, int H, int I, int k, int NT,
-                                                       int RT, SelectArgs sa, GroupOut o, uint16_t *__restrict__ hhi,
-                                                       uint16_t *__restrict__ hlo) {
+                                                       int RT, SelectArgs sa, GroupOut o, int hot_only,
+                                                       uint16_t *__restrict__ hhi, uint16_t *__restrict__ hlo) {
     extern __shared__ __align__(16) char smem[];
     __shared__ int sid[kFusedSelectPairs], sflag[kFusedSelectPairs], spl[kSmallRouteTokens], sinfo[4];
     // the residency table borrows the start of the token staging area, which
@@ -246,6 +246,8 @@ __global__ __launch_bounds__(512) void ffn_gate_up_sel(const uint16_t *__restric
     const int n = sinfo[0];
     const uint8_t *base = reinterpret_cast<const uint8_t *>(((uint64_t)(uint32_t)sinfo[3] << 32) | (uint32_t)sinfo[2]);
     if (n == 0 || base == nullptr) return;
+    // hot_only: an expert read from a scratch slot is left to the cold part
+    if (hot_only && base >= sa.scratch && base < sa.scratch + (size_t)sa.n_cold * sa.blob_bytes) return;
     gate_up_tile_blk<SPW>(x, H, I, k, NT, RT, base, n, sinfo[1], [&](int c) { return spl[c]; }, smem, hhi, hlo);
 }
 
@@ -885,33 +887,50 @@ void launch_combine(const FfnArgs &a, const float *y, hipStream_t st) {
 }  // namespace
 
 template <int SPW, int NPL>
-void launch_gate_up_sel(const FfnArgs &a, int RT, const SelectArgs &sa, const GroupOut &o, uint16_t *hhi,
-                        uint16_t *hlo, int umax, hipStream_t st) {
+void launch_gate_up_sel(const FfnArgs &a, int RT, const SelectArgs &sa, const GroupOut &o, int hot_only,
+                        uint16_t *hhi, uint16_t *hlo, int umax, hipStream_t st) {
     const int slices = a.H / 128 / SPW;
     const int row_bytes = (a.H / 8 + 1) * 16;
     const int NT = stage_rows(row_bytes, RT == 2 ? kStageBytesWide : kStageBytes);
     const size_t lds = (size_t)NT * row_bytes + (size_t)2 * RT * slices * 64 * 16;
     MOE_LAUNCH("ffn_gate_up_sel", (ffn_gate_up_sel<SPW, NPL>), dim3(a.I / (16 * RT), umax),
-               dim3(128 * RT * slices), lds, st, a.x, a.H, a.I, a.k, NT, RT, sa, o, hhi, hlo);
+               dim3(128 * RT * slices), lds, st, a.x, a.H, a.I, a.k, NT, RT, sa, o, hot_only, hhi, hlo);
 }
 
 template <int SPW>
-void gate_up_sel_npl(int npl, const FfnArgs &a, int RT, const SelectArgs &sa, const GroupOut &o, uint16_t *hhi,
-                     uint16_t *hlo, int umax, hipStream_t st) {
+void gate_up_sel_npl(int npl, const FfnArgs &a, int RT, const SelectArgs &sa, const GroupOut &o, int hot_only,
+                     uint16_t *hhi, uint16_t *hlo, int umax, hipStream_t st) {
     switch (npl) {
-        case 1: launch_gate_up_sel<SPW, 1>(a, RT, sa, o, hhi, hlo, umax, st); break;
-        case 2: launch_gate_up_sel<SPW, 2>(a, RT, sa, o, hhi, hlo, umax, st); break;
-        case 4: launch_gate_up_sel<SPW, 4>(a, RT, sa, o, hhi, hlo, umax, st); break;
-        case 8: launch_gate_up_sel<SPW, 8>(a, RT, sa, o, hhi, hlo, umax, st); break;
-        default: launch_gate_up_sel<SPW, 16>(a, RT, sa, o, hhi, hlo, umax, st); break;
+        case 1: launch_gate_up_sel<SPW, 1>(a, RT, sa, o, hot_only, hhi, hlo, umax, st); break;
+        case 2: launch_gate_up_sel<SPW, 2>(a, RT, sa, o, hot_only, hhi, hlo, umax, st); break;
+        case 4: launch_gate_up_sel<SPW, 4>(a, RT, sa, o, hot_only, hhi, hlo, umax, st); break;
+        case 8: launch_gate_up_sel<SPW, 8>(a, RT, sa, o, hot_only, hhi, hlo, umax, st); break;
+        default: launch_gate_up_sel<SPW, 16>(a, RT, sa, o, hot_only, hhi, hlo, umax, st); break;
     }
 }
 
-bool ffn_select_fusable(int T, int k, int H, int I) {
+// The gate/up launch with the selection in every block, for every expert or
+// (hot_only) the HBM-resident ones.
+static void gate_up_sel(const FfnArgs &a, const SelectArgs &sa, const GroupOut &o, int hot_only, uint16_t *hhi,
+                 uint16_t *hlo, int umax, hipStream_t st) {
+    const int npl = topk_npl(a.E);
+    const GateUpShape gs = gate_up_shape(a.T, a.H);
+    switch (gs.spw) {
+        case 1: gate_up_sel_npl<1>(npl, a, gs.rt, sa, o, hot_only, hhi, hlo, umax, st); break;
+        case 2: gate_up_sel_npl<2>(npl, a, gs.rt, sa, o, hot_only, hhi, hlo, umax, st); break;
+        case 4: gate_up_sel_npl<4>(npl, a, gs.rt, sa, o, hot_only, hhi, hlo, umax, st); break;
+        case 8: gate_up_sel_npl<8>(npl, a, gs.rt, sa, o, hot_only, hhi, hlo, umax, st); break;
+        default: gate_up_sel_npl<16>(npl, a, gs.rt, sa, o, hot_only, hhi, hlo, umax, st); break;
+    }
+}
+
+bool ffn_select_fusable(int T, int k, int E, int H, int I) {
     if (!ffn_block_path(T, H, I)) return false;
     const GateUpShape g = gate_up_shape(T, H);
     const int P = T * k, threads = 128 * g.rt * g.slices;
-    return P <= kFusedSelectPairs && P <= threads;
+    // the block selection takes one pair per thread and two residency
+    // entries per thread
+    return P <= kFusedSelectMaxPairs && P <= threads && E <= 2 * threads;
 }
 
 bool ffn_block_path(int T, int H, int I) {
@@ -970,21 +989,28 @@ hipError_t launch_ffn_select(const FfnArgs &a, const float *z, int renorm, int32
     uint16_t *hhi = reinterpret_cast<uint16_t *>(ws + L.hbuf);
     uint16_t *hlo = hhi + P * (size_t)a.I;
     float *y = reinterpret_cast<float *>(ws + L.ybuf);
-    const int npl = topk_npl(a.E);
-    const GateUpShape gs = gate_up_shape(a.T, a.H);
-    switch (gs.spw) {
-        case 1: gate_up_sel_npl<1>(npl, a, gs.rt, sa, o, hhi, hlo, umax, st); break;
-        case 2: gate_up_sel_npl<2>(npl, a, gs.rt, sa, o, hhi, hlo, umax, st); break;
-        case 4: gate_up_sel_npl<4>(npl, a, gs.rt, sa, o, hhi, hlo, umax, st); break;
-        case 8: gate_up_sel_npl<8>(npl, a, gs.rt, sa, o, hhi, hlo, umax, st); break;
-        default: gate_up_sel_npl<16>(npl, a, gs.rt, sa, o, hhi, hlo, umax, st); break;
-    }
+    gate_up_sel(a, sa, o, 0, hhi, hlo, umax, st);
     if (down_combine_lds(a.T, a.k, a.H, a.I)) {
         launch_down_combine(a, gv, hhi, hlo, st);
     } else {
         down_blk(a, gv, kPartAll, hhi, hlo, y, umax, st);
         launch_combine(a, y, st);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_ffn_select_hot(const FfnArgs &a, const float *z, int renorm, int32_t *ids, float *w,
+                                 const GroupArgs &g, char *ws, const WsLayout &L, hipStream_t st) {
+    const GroupView gv = group_view(ws, L);
+    const GroupOut o = GroupOut::at(ws, L);
+    const SelectArgs sa = select_args(z, a.T, a.k, renorm, ids, w, g);
+    const size_t P = (size_t)a.T * a.k;
+    const int umax = (int)((size_t)a.E < P ? (size_t)a.E : P);
+    uint16_t *hhi = reinterpret_cast<uint16_t *>(ws + L.hbuf);
+    uint16_t *hlo = hhi + P * (size_t)a.I;
+    float *y = reinterpret_cast<float *>(ws + L.ybuf);
+    gate_up_sel(a, sa, o, 1, hhi, hlo, umax, st);
+    if (!down_combine_lds(a.T, a.k, a.H, a.I)) down_blk(a, gv, kPartHot, hhi, hlo, y, umax, st);
     return hipGetLastError();
 }
 

@@ -16,6 +16,7 @@
 // running beside it (the hot experts' FFN during a layer's gather) started
 // 50-170 us late and ran up to five times slower; at 256 KB it starts within
 // about 20 us and runs 10-40% longer than alone.
+#include "device_util.hpp"
 #include "kernels.hpp"
 
 namespace moe {
@@ -50,6 +51,89 @@ __global__ __launch_bounds__(kGatherThreads) void gather_cold(const uint8_t *__r
             }
         }
     }
+}
+
+// Decode variant that does not wait for a grouping launch: every block takes
+// the top-k of the T tokens from the logits itself (the same wave top-k as
+// the FFN kernels, so the same picks), marks the picked experts, lists the
+// cold ones in increasing expert order, then copies them as gather_cold does.
+// T*k <= kMaxPairsSel; every list index stays below m <= min(E, T*k).
+constexpr int kMaxPairsSel = 1024;
+
+template <int NPL>
+__global__ __launch_bounds__(kGatherThreads) void gather_cold_sel(const float *__restrict__ z, int T, int E, int k,
+                                                                  const int32_t *__restrict__ slot, int n_cold,
+                                                                  const uint8_t *__restrict__ host_cold,
+                                                                  uint8_t *__restrict__ scratch, size_t blob_bytes) {
+    __shared__ uint8_t picked[kMaxExperts];
+    __shared__ int32_t list[kMaxPairsSel];
+    __shared__ int32_t count;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int e = tid; e < E; e += kGatherThreads) picked[e] = 0;
+    __syncthreads();
+    for (int t = wave; t < T; t += kGatherThreads / 64) {
+        int pe;
+        float pw;
+        topk_wave<NPL>(z + (size_t)t * E, E, k, 1, &pe, &pw);
+        if (lane < k) picked[pe] = 1;
+    }
+    __syncthreads();
+    if (wave == 0) {   // picked cold experts in increasing order, by ballots over 64 experts at a time
+        int m = 0;
+        for (int e0 = 0; e0 < E; e0 += 64) {
+            const int e = e0 + lane;
+            int c = -1;
+            if (e < E && picked[e]) {
+                const int sv = slot[e];
+                if (sv < 0 && -sv - 1 < n_cold) c = -sv - 1;
+            }
+            const uint64_t b = __ballot(c >= 0);
+            const int before = __popcll(b & ((1ull << lane) - 1ull));
+            if (c >= 0) list[m + before] = c;
+            m += __popcll(b);
+        }
+        if (lane == 0) count = m;
+    }
+    __syncthreads();
+    const int m = count;
+    const size_t units = blob_bytes / 16;
+    const size_t per_iter = (size_t)kGatherThreads * kGatherUnroll;
+    for (int i = 0; i < m; ++i) {
+        const int c = list[i];
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(host_cold + (size_t)c * blob_bytes);
+        u32x4 *dst = reinterpret_cast<u32x4 *>(scratch + (size_t)c * blob_bytes);
+        for (size_t base = (size_t)blockIdx.x * per_iter; base < units; base += (size_t)gridDim.x * per_iter) {
+            u32x4 v[kGatherUnroll];
+#pragma unroll
+            for (int j = 0; j < kGatherUnroll; ++j) {
+                const size_t u = base + (size_t)j * kGatherThreads + threadIdx.x;
+                if (u < units) v[j] = __builtin_nontemporal_load(src + u);
+            }
+#pragma unroll
+            for (int j = 0; j < kGatherUnroll; ++j) {
+                const size_t u = base + (size_t)j * kGatherThreads + threadIdx.x;
+                if (u < units) dst[u] = v[j];
+            }
+        }
+    }
+}
+
+hipError_t launch_gather_sel(const float *z, int T, int E, int k, const int32_t *slot, int n_cold,
+                             const uint8_t *host_cold, uint8_t *scratch, size_t blob_bytes, hipStream_t st) {
+    if (T * k > kMaxPairsSel || E > kMaxExperts) return hipErrorInvalidValue;
+    const size_t units = blob_bytes / 16;
+    const size_t per_iter = (size_t)kGatherThreads * kGatherUnroll;
+    size_t blocks = (units + per_iter - 1) / per_iter;
+    if (blocks > kGatherBlocks) blocks = kGatherBlocks;
+    const dim3 g((unsigned)blocks), b(kGatherThreads);
+    switch (topk_npl(E)) {
+        case 1: MOE_LAUNCH("gather_cold", gather_cold_sel<1>, g, b, 0, st, z, T, E, k, slot, n_cold, host_cold, scratch, blob_bytes); break;
+        case 2: MOE_LAUNCH("gather_cold", gather_cold_sel<2>, g, b, 0, st, z, T, E, k, slot, n_cold, host_cold, scratch, blob_bytes); break;
+        case 4: MOE_LAUNCH("gather_cold", gather_cold_sel<4>, g, b, 0, st, z, T, E, k, slot, n_cold, host_cold, scratch, blob_bytes); break;
+        case 8: MOE_LAUNCH("gather_cold", gather_cold_sel<8>, g, b, 0, st, z, T, E, k, slot, n_cold, host_cold, scratch, blob_bytes); break;
+        default: MOE_LAUNCH("gather_cold", gather_cold_sel<16>, g, b, 0, st, z, T, E, k, slot, n_cold, host_cold, scratch, blob_bytes); break;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_gather(const uint8_t *host_cold, uint8_t *scratch, size_t blob_bytes, const int32_t *slot,

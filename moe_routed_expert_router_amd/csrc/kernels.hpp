@@ -60,6 +60,11 @@ hipError_t launch_gather(const uint8_t *host_cold, uint8_t *scratch, size_t blob
                          const int32_t *slot, const char *ws, const WsLayout &L,
                          hipStream_t st);
 
+// Decode gather that takes the top-k from the logits z [T][E] itself (no
+// grouping launch before it): copies the picked cold experts host -> scratch.
+hipError_t launch_gather_sel(const float *z, int T, int E, int k, const int32_t *slot, int n_cold,
+                             const uint8_t *host_cold, uint8_t *scratch, size_t blob_bytes, hipStream_t st);
+
 // Grouped SwiGLU FFN over the grouped pairs and the weighted combine into out.
 struct FfnArgs {
     const uint16_t *x;
@@ -84,12 +89,28 @@ hipError_t launch_ffn_part(const FfnArgs &a, int part, int umax_part, char *ws, 
 // and the grouping in every block (block 0 publishes ids, w and the pick set),
 // then down and combine as in launch_ffn.  Needs ffn_select_fusable.
 constexpr int kFusedSelectPairs = 512;
+// Pairs up to which the layer uses the gate/up kernel that selects in every
+// block.  The per-block selection grows with T while the launch it saves
+// does not: measured per layer (4 layers rotating, graph replay), it wins at
+// one token (34 against 35.5 us all resident, 50.5 against 53 us hot/cold)
+// and loses from two tokens on (all resident: 58 against 54 us at T = 2, 155
+// against 111 at T = 8, 848 against 256 at T = 32).
+constexpr int kFusedSelectMaxPairs = 8;
 hipError_t launch_ffn_select(const FfnArgs &a, const float *z, int renorm, int32_t *ids, float *w,
                              const GroupArgs &g, char *ws, const WsLayout &L, hipStream_t st);
 
+// Decode layer with cold experts: the hot experts' gate/up (and, past the
+// fused down + combine sizes, their down) with the selection recomputed in
+// every block as in launch_ffn_select; block 0 publishes ids, w and the whole
+// pick set, so launch_ffn_part(kPartCold) can follow once the gather is done.
+// Needs ffn_select_fusable.
+hipError_t launch_ffn_select_hot(const FfnArgs &a, const float *z, int renorm, int32_t *ids, float *w,
+                                 const GroupArgs &g, char *ws, const WsLayout &L, hipStream_t st);
+
 // True when launch_ffn_select applies (block path, T*k within both the
-// selection's LDS and the gate/up block's threads).
-bool ffn_select_fusable(int T, int k, int H, int I);
+// selection's LDS and the gate/up block's threads, E within two entries per
+// thread).
+bool ffn_select_fusable(int T, int k, int E, int H, int I);
 
 // True when launch_ffn uses the block kernels (decode sizes).
 bool ffn_block_path(int T, int H, int I);

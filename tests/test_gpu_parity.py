@@ -373,6 +373,33 @@ def test_max_experts_and_k():
     check_out(out.cpu().numpy(), oracle_out(L)["out"])
 
 
+@pytest.mark.parametrize("cold", [False, True])
+def test_many_experts_few_pairs(cold):
+    """E = 1024 with few pairs and a small hidden size: the decode launches
+    whose blocks would hold fewer threads than half the residency entries
+    take the grouped path instead; routing and outputs as the oracle's,
+    hot/cold bit-identical to all resident."""
+    wl = gen.Workload("manyE", 128, 128, 1024, 2, 5)
+    hot = list(range(0, 1024, 2)) if cold else None
+    L = Layer(wl, hot=hot)
+    ref_layer = Layer(wl) if cold else None
+    try:
+        ids_g, w_g, z_g = route_on_gpu(L)
+        check_route(L, ids_g, w_g, z_g)
+        out = L.forward()
+        torch.cuda.synchronize()
+        check_out(out.cpu().numpy(), oracle_out(L)["out"])
+        if cold:
+            assert len(ogather.picked_cold(L.ids.cpu().numpy(), L.slot_np)) > 0
+            ref = ref_layer.forward()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref)
+    finally:
+        L.close()
+        if ref_layer is not None:
+            ref_layer.close()
+
+
 def test_k1_single_expert():
     wl = gen.Workload("k1", 256, 128, 8, 1, 6)
     L = Layer(wl)
