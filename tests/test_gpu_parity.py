@@ -375,11 +375,12 @@ def test_max_experts_and_k():
 
 @pytest.mark.parametrize("cold", [False, True])
 def test_many_experts_few_pairs(cold):
-    """E = 1024 with few pairs and a small hidden size: the decode launches
-    whose blocks would hold fewer threads than half the residency entries
-    take the grouped path instead; routing and outputs as the oracle's,
-    hot/cold bit-identical to all resident."""
-    wl = gen.Workload("manyE", 128, 128, 1024, 2, 5)
+    """E = 1024 with 8 pairs (the one-token launch sequences' limit) and a
+    small hidden size: the decode launches whose blocks would hold fewer
+    threads than half the residency entries take the grouped path instead;
+    routing and outputs as the oracle's, hot/cold bit-identical to all
+    resident."""
+    wl = gen.Workload("manyE", 128, 128, 1024, 2, 4)
     hot = list(range(0, 1024, 2)) if cold else None
     L = Layer(wl, hot=hot)
     ref_layer = Layer(wl) if cold else None
@@ -487,7 +488,8 @@ def test_gpu_error_paths():
     assert st == moe.MOE_ERR_MISALIGNED
 
 
-@pytest.mark.parametrize("name,T,delta", [("tiny", 8, 0.0), ("hotcold8", 8, 0.0), ("hotcold8", 32, 3.0)])
+@pytest.mark.parametrize("name,T,delta", [("tiny", 8, 0.0), ("hotcold8", 8, 0.0), ("hotcold8", 32, 3.0),
+                                          ("hotcold8", 1, 3.0), ("hotcold8", 1, 0.0)])
 def test_graph_replay_matches_eager(name, T, delta):
     """The layer captured in a HIP graph gives the eager result on every
     replay, with eager work and synchronisations between replays (with cold
