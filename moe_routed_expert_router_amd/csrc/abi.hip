@@ -138,8 +138,8 @@ moe::GroupArgs group_args(const moe_shape *s, int32_t T, const int32_t *ids, con
     return g;
 }
 
-moe_status enqueue_ffn(const moe_shape *s, int32_t T, const uint16_t *x, const int32_t *ids, const float *w,
-                       int32_t out_dtype, void *out, char *ws, const moe::WsLayout &L, hipStream_t st) {
+moe::FfnArgs ffn_args(const moe_shape *s, int32_t T, const uint16_t *x, const int32_t *ids, const float *w,
+                      int32_t out_dtype, void *out) {
     moe::FfnArgs a;
     a.x = x;
     a.ids = ids;
@@ -151,7 +151,12 @@ moe_status enqueue_ffn(const moe_shape *s, int32_t T, const uint16_t *x, const i
     a.k = s->top_k;
     a.out_bf16 = out_dtype == MOE_OUT_BF16;
     a.out = out;
-    return hip_status(moe::launch_ffn(a, ws, L, st), "ffn launch");
+    return a;
+}
+
+moe_status enqueue_ffn(const moe_shape *s, int32_t T, const uint16_t *x, const int32_t *ids, const float *w,
+                       int32_t out_dtype, void *out, char *ws, const moe::WsLayout &L, hipStream_t st) {
+    return hip_status(moe::launch_ffn(ffn_args(s, T, x, ids, w, out_dtype, out), ws, L, st), "ffn launch");
 }
 
 // Per-device side stream on which moe_layer_forward runs the cold gather while
@@ -399,37 +404,19 @@ moe_status moe_layer_forward(const moe_shape *s, int32_t T, const uint16_t *x, c
     const bool direct = direct_read(r);
     if (T <= moe::kSmallRouteTokens && (r->n_cold == 0 || direct) && moe::ffn_select_fusable(T, k, E, H, s->inter)) {
         // no cold expert to gather: the gate/up kernel selects and groups by itself
-        moe::FfnArgs a;
-        a.x = x;
-        a.ids = topk_ids;
-        a.w = topk_w;
-        a.T = T;
-        a.H = H;
-        a.I = s->inter;
-        a.E = E;
-        a.k = k;
-        a.out_bf16 = out_dtype == MOE_OUT_BF16;
-        a.out = out;
+        const moe::FfnArgs a = ffn_args(s, T, x, topk_ids, topk_w, out_dtype, out);
         TRY(hip_status(moe::launch_ffn_select(a, z, renormalize != 0, topk_ids, topk_w, g, w, L, st),
                        "select + ffn launch"));
         return ok();
     }
-    if (T <= moe::kSmallRouteTokens && r->n_cold > 0 && !direct && moe::ffn_select_fusable(T, k, E, H, s->inter)) {
-        // decode with cold experts, no grouping launch: the gather (side
-        // stream) and the hot experts' gate/up (caller's stream) each take the
-        // top-k from the logits themselves; the cold experts' FFN and the
-        // combine follow the join, reading the pick set the gate/up published
-        moe::FfnArgs a;
-        a.x = x;
-        a.ids = topk_ids;
-        a.w = topk_w;
-        a.T = T;
-        a.H = H;
-        a.I = s->inter;
-        a.E = E;
-        a.k = k;
-        a.out_bf16 = out_dtype == MOE_OUT_BF16;
-        a.out = out;
+    if (T <= moe::kSmallRouteTokens && r->n_cold > 0 && !direct && moe::ffn_block_path(T, H, s->inter)) {
+        // decode with cold experts: the gather, forked right after the router,
+        // takes the top-k from the logits itself on the side stream, so it
+        // waits for no grouping; the hot experts' FFN runs meanwhile on the
+        // caller's stream (at one token its gate/up selects in every block
+        // and publishes the pick set, else one select-and-group launch comes
+        // first); the cold experts' FFN and the combine follow the join
+        const moe::FfnArgs a = ffn_args(s, T, x, topk_ids, topk_w, out_dtype, out);
         const int P = T * k;
         std::unique_lock<std::mutex> lock;
         SideStream *side = nullptr;
@@ -440,8 +427,14 @@ moe_status moe_layer_forward(const moe_shape *s, int32_t T, const uint16_t *x, c
                                               side->st),
                        "gather launch"));
         TRY(hip_status(hipEventRecord(side->join, side->st), "gather join"));
-        TRY(hip_status(moe::launch_ffn_select_hot(a, z, renormalize != 0, topk_ids, topk_w, g, w, L, st),
-                       "hot ffn launch"));
+        if (moe::ffn_select_fusable(T, k, E, H, s->inter)) {
+            TRY(hip_status(moe::launch_ffn_select_hot(a, z, renormalize != 0, topk_ids, topk_w, g, w, L, st),
+                           "hot ffn launch"));
+        } else {
+            TRY(hip_status(moe::launch_select_group_small(z, T, k, renormalize != 0, topk_ids, topk_w, g, w, L, st),
+                           "select-and-group launch"));
+            TRY(hip_status(moe::launch_ffn_part(a, moe::kPartHot, E < P ? E : P, w, L, st), "hot ffn launch"));
+        }
         TRY(hip_status(hipStreamWaitEvent(st, side->join, 0), "gather join"));
         lock.unlock();
         TRY(hip_status(moe::launch_ffn_part(a, moe::kPartCold, r->n_cold < P ? r->n_cold : P, w, L, st),
@@ -454,37 +447,6 @@ moe_status moe_layer_forward(const moe_shape *s, int32_t T, const uint16_t *x, c
     } else {
         TRY(hip_status(moe::launch_topk(z, T, E, k, renormalize != 0, topk_ids, topk_w, st), "top-k launch"));
         TRY(hip_status(moe::launch_group(g, w, L, st), "pick-set launch"));
-    }
-    if (r->n_cold > 0 && !direct && moe::ffn_block_path(T, H, s->inter)) {
-        // the hot experts' FFN needs nothing from the gather: it runs on the
-        // caller's stream while the side stream copies the cold experts in;
-        // the cold experts' FFN and the combine follow the join
-        moe::FfnArgs a;
-        a.x = x;
-        a.ids = topk_ids;
-        a.w = topk_w;
-        a.T = T;
-        a.H = H;
-        a.I = s->inter;
-        a.E = E;
-        a.k = k;
-        a.out_bf16 = out_dtype == MOE_OUT_BF16;
-        a.out = out;
-        const int P = T * k;
-        std::unique_lock<std::mutex> lock;
-        SideStream *side = nullptr;
-        TRY(side_stream(lock, &side));
-        TRY(hip_status(hipEventRecord(side->fork, st), "gather fork"));
-        TRY(hip_status(hipStreamWaitEvent(side->st, side->fork, 0), "gather fork"));
-        TRY(hip_status(moe::launch_gather(r->host_cold, r->scratch, g.blob_bytes, r->slot, w, L, side->st),
-                       "gather launch"));
-        TRY(hip_status(hipEventRecord(side->join, side->st), "gather join"));
-        TRY(hip_status(moe::launch_ffn_part(a, moe::kPartHot, E < P ? E : P, w, L, st), "hot ffn launch"));
-        TRY(hip_status(hipStreamWaitEvent(st, side->join, 0), "gather join"));
-        lock.unlock();
-        TRY(hip_status(moe::launch_ffn_part(a, moe::kPartCold, r->n_cold < P ? r->n_cold : P, w, L, st),
-                       "cold ffn launch"));
-        return ok();
     }
     if (r->n_cold > 0 && !direct)
         TRY(hip_status(moe::launch_gather(r->host_cold, r->scratch, g.blob_bytes, r->slot, w, L, st),
