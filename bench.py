@@ -946,50 +946,61 @@ def main():
     torch.cuda.empty_cache()
 
     extra = {}
-    if not a.no_batch8 and a.workload == "decode1":
-        log("[bench] secondary: hotcold8 (batch 8, 255 hot / 129 cold)")
+
+    def secondary(key, title, fn):
+        """One secondary figure; a host-side failure (say, no more pinned
+        memory on this host) is recorded in its place and the run goes on."""
+        log(f"[bench] secondary: {title}")
+        try:
+            extra[key] = fn()
+        except Exception as e:   # noqa: BLE001 - reported in the JSON line
+            log(f"[bench] secondary {key} failed: {type(e).__name__}: {e}")
+            extra[key] = {"error": f"{type(e).__name__}: {e}"}
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+
+    def batch8():
         w8, s8, st8, g8, p8, b8 = measure("hotcold8", 128, 8, 16, not a.no_graph, 64)
-        k8 = kernel_table(p8, b8)
-        ffn8_us = role_us(p8, "gate_up") + role_us(p8, "down") + role_us(p8, "combine")
-        entry = {"tokens_per_s": round(st8 * 8 / s8, 1), "ms_per_step": round(1e3 * s8 / st8, 4),
-                 "graph": g8, "mean_distinct_experts": round(b8["unique"], 2),
-                 "ffn_hbm_GB_per_s": round((b8["gate_up"] + b8["down"]) / (ffn8_us * 1e-6) / 1e9, 1),
-                 "kernels": k8}
-        if "gather_cold" in p8 and b8["gather_cold"] > 0:
-            entry["gather_link_GB_per_s"] = round(b8["gather_cold"] / (role_us(p8, "gather_cold") * 1e-6) / 1e9, 2)
-            entry["gather_bytes_per_step"] = int(b8["gather_cold"])
-        extra["batch8_hotcold"] = entry
-        w8.close()
-        del w8
-        torch.cuda.empty_cache()
+        try:
+            k8 = kernel_table(p8, b8)
+            ffn8_us = role_us(p8, "gate_up") + role_us(p8, "down") + role_us(p8, "combine")
+            entry = {"tokens_per_s": round(st8 * 8 / s8, 1), "ms_per_step": round(1e3 * s8 / st8, 4),
+                     "graph": g8, "mean_distinct_experts": round(b8["unique"], 2),
+                     "ffn_hbm_GB_per_s": round((b8["gate_up"] + b8["down"]) / (ffn8_us * 1e-6) / 1e9, 1),
+                     "kernels": k8}
+            if "gather_cold" in p8 and b8["gather_cold"] > 0:
+                entry["gather_link_GB_per_s"] = round(b8["gather_cold"] / (role_us(p8, "gather_cold") * 1e-6) / 1e9,
+                                                      2)
+                entry["gather_bytes_per_step"] = int(b8["gather_cold"])
+            return entry
+        finally:
+            w8.close()
+            torch.cuda.empty_cache()
 
-    if not a.no_direct_read and a.workload == "decode1":
-        log("[bench] secondary: gather-then-compute vs direct read of cold experts (batch 1/8/32)")
-        extra["direct_read"] = measure_direct_read()
-
-    if not a.no_adaptive and a.workload == "decode1":
-        log("[bench] secondary: adaptive residency on drifting traffic")
-        extra["adaptive_residency"] = {"drifted_once": measure_adaptive(),
-                                       "drifting": measure_adaptive(drift_every=250)}
-
-    if not a.no_verify and a.workload == "decode1":
-        log("[bench] secondary: speculative-verify steps (streams x (1 + draft), correlated windows)")
-        extra["verify"] = measure_verify()
-
-    if not a.no_layer_copy and a.workload == "decode1":
-        log("[bench] secondary: layer-granular copy baseline (all 384 experts of a layer from the host)")
-        extra["layer_copy"] = measure_layer_copy()
-
-    if not a.no_ffn_batches and a.workload == "decode1":
-        log("[bench] secondary: grouped FFN alone at batch 1/8/32 (all experts resident)")
-        extra["ffn_by_batch"] = measure_ffn_batches()
-
-    if not a.no_step40 and a.workload == "decode1":
-        log("[bench] secondary: step40 (40 layers, batch 32, 255 hot / 129 cold, shared scratch)")
-        extra["step40_batch32"] = measure_stack("step40", 10, 2, not a.no_graph, one_token_rows=16)
-        lc, st = extra.get("layer_copy"), extra["step40_batch32"]
-        if lc and "tokens_per_s" in st:
-            lc["picked_only_over_layer_copy"] = round(st["tokens_per_s"] / lc["tokens_per_s"], 1)
+    if a.workload == "decode1":
+        if not a.no_batch8:
+            secondary("batch8_hotcold", "hotcold8 (batch 8, 255 hot / 129 cold)", batch8)
+        if not a.no_direct_read:
+            secondary("direct_read", "gather-then-compute vs direct read of cold experts (batch 1/8/32)",
+                      measure_direct_read)
+        if not a.no_adaptive:
+            secondary("adaptive_residency", "adaptive residency on drifting traffic",
+                      lambda: {"drifted_once": measure_adaptive(), "drifting": measure_adaptive(drift_every=250)})
+        if not a.no_verify:
+            secondary("verify", "speculative-verify steps (streams x (1 + draft), correlated windows)",
+                      measure_verify)
+        if not a.no_layer_copy:
+            secondary("layer_copy", "layer-granular copy baseline (all 384 experts of a layer from the host)",
+                      measure_layer_copy)
+        if not a.no_ffn_batches:
+            secondary("ffn_by_batch", "grouped FFN alone at batch 1/8/32 (all experts resident)",
+                      measure_ffn_batches)
+        if not a.no_step40:
+            secondary("step40_batch32", "step40 (40 layers, batch 32, 255 hot / 129 cold, shared scratch)",
+                      lambda: measure_stack("step40", 10, 2, not a.no_graph, one_token_rows=16))
+            lc, st = extra.get("layer_copy"), extra["step40_batch32"]
+            if lc and "tokens_per_s" in lc and "tokens_per_s" in st:
+                lc["picked_only_over_layer_copy"] = round(st["tokens_per_s"] / lc["tokens_per_s"], 1)
 
     cpu = None
     if not a.no_cpu_baseline:
