@@ -638,6 +638,73 @@ def measure_direct_read(batches=(1, 8, 32), layers: int = 4, reps: int = 8) -> d
     return out
 
 
+def pcie_link() -> dict:
+    """Negotiated PCIe speed and width of GPU 0, from sysfs (empty when not
+    readable)."""
+    import torch
+    try:
+        pr = torch.cuda.get_device_properties(0)
+        bdf = f"{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:{pr.pci_device_id:02x}.0"
+        base = f"/sys/bus/pci/devices/{bdf}"
+        out = {"bdf": bdf}
+        for f in ("current_link_speed", "current_link_width", "max_link_speed", "max_link_width"):
+            with open(os.path.join(base, f)) as fh:
+                out[f] = fh.read().strip()
+        return out
+    except Exception as e:   # noqa: BLE001 - informational only
+        return {"unavailable": f"{type(e).__name__}: {e}"}
+
+
+def measure_gather_sweep(ms=(1, 2, 4, 8, 16, 64, 129), reps: int = 5) -> dict:
+    """The cold gather alone with exactly m distinct cold experts picked
+    (ids padded with hot experts), on a hot/cold decode layer: link GB/s =
+    m * B / kernel time, beside the DMA engines copying the same bytes from
+    pinned host memory (the practical ceiling) and the PCIe link's
+    negotiated speed and width."""
+    import torch
+    import moe_routed_expert_router_amd as moe
+    from synth import gen
+    from tests.gpu_setup import Layer
+    wl = gen.workload("hotcold8")
+    k = wl.top_k
+    L = Layer(wl, T=max(-(-m // k) for m in ms))
+    out = {"link": pcie_link(), "peak_GB_per_s": LINK_PEAK_GBS}
+    src = torch.empty(max(ms) * L.B, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty_like(src, device="cuda")
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(reps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / reps
+
+    try:
+        for m in ms:
+            T = -(-m // k)
+            pad = L.cold[:m] + [L.hot[0]] * (T * k - m)
+            ids = torch.tensor(pad, dtype=torch.int32, device="cuda").reshape(T, k)
+            ws = torch.empty(moe.moe_workspace_bytes(L.shape, T), dtype=torch.uint8, device="cuda")
+            ms_k = timed(lambda: moe.moe_gather_cold(L.shape, ids, L.residency, ws))
+            n = m * L.B
+            ms_d = timed(lambda: dst[:n].copy_(src[:n], non_blocking=True))
+            out[f"m{m}"] = {"bytes": n, "kernel_us": round(1e3 * ms_k, 1),
+                            "kernel_GB_per_s": round(n / ms_k / 1e6, 2),
+                            "dma_GB_per_s": round(n / ms_d / 1e6, 2),
+                            "frac_of_link": round(n / ms_k / 1e6 / LINK_PEAK_GBS, 3)}
+            log(f"[bench] gather m={m:3d}: {1e3 * ms_k:9.1f} us, {n / ms_k / 1e6:5.1f} GB/s "
+                f"(DMA {n / ms_d / 1e6:5.1f} GB/s)")
+        return out
+    finally:
+        L.close()
+        del src, dst
+        torch.cuda.empty_cache()
+
+
 def measure_layer_copy(T: int = 32, layers: int = 40, reps: int = 3) -> dict:
     """Layer-granular copy baseline: the layer's whole expert set (all 384
     experts, 5.13 GB, kept in pinned host memory as a layer offloader keeps
@@ -859,6 +926,7 @@ def main():
     ap.add_argument("--primary-only", action="store_true", help="skip every secondary figure")
     ap.add_argument("--no-adaptive", action="store_true", help="skip the adaptive-residency secondary figures")
     ap.add_argument("--no-verify", action="store_true", help="skip the speculative-verify secondary figures")
+    ap.add_argument("--no-gather-sweep", action="store_true", help="skip the gather-alone sweep over m")
     ap.add_argument("--no-layer-copy", action="store_true",
                     help="skip the whole-layer cold copy baseline")
     ap.add_argument("--no-direct-read", action="store_true",
@@ -872,7 +940,7 @@ def main():
     a = ap.parse_args()
     if a.primary_only:
         for k in ("no_batch8", "no_adaptive", "no_verify", "no_layer_copy", "no_direct_read", "no_ffn_batches",
-                  "no_step40"):
+                  "no_step40", "no_gather_sweep"):
             setattr(a, k, True)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -989,6 +1057,9 @@ def main():
         if not a.no_verify:
             secondary("verify", "speculative-verify steps (streams x (1 + draft), correlated windows)",
                       measure_verify)
+        if not a.no_gather_sweep:
+            secondary("gather_sweep", "cold gather alone, m = 1..129 picked cold experts, beside DMA copies",
+                      measure_gather_sweep)
         if not a.no_layer_copy:
             secondary("layer_copy", "layer-granular copy baseline (all 384 experts of a layer from the host)",
                       measure_layer_copy)
