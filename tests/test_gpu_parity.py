@@ -182,7 +182,7 @@ def boost_cold(L, delta):
     L.bias.copy_(torch.from_numpy(L.bias_np))
 
 
-@pytest.mark.parametrize("T,delta", [(32, 3.0), (5, 3.0), (32, 0.0), (1, 3.0)])
+@pytest.mark.parametrize("T,delta", [(32, 3.0), (5, 3.0), (32, 0.0), (1, 3.0), (1, 40.0), (8, 40.0)])
 def test_decode_cold_picks_overlapped(T, delta):
     """Decode layer with many picked cold experts: the gather runs on the side
     stream while the hot experts' FFN runs; ids, gathered bytes and outputs
@@ -203,6 +203,8 @@ def test_decode_cold_picks_overlapped(T, delta):
         print(f"T={T} delta={delta}: picked cold {len(pc)}", flush=True)
         if delta > 0:
             assert len(pc) >= min(3, T)
+        if delta >= 40:   # every pick cold: the HBM-resident part has nothing to do
+            assert len(pc) == len(np.unique(ids))
         assert torch.equal(L.ids, hot.ids)
         assert torch.equal(a, b), "hot/cold placement changed the output bits"
         host = L.host.np.reshape(L.n_cold, L.B)
