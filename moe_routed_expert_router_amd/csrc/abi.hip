@@ -409,13 +409,31 @@ moe_status moe_layer_forward(const moe_shape *s, int32_t T, const uint16_t *x, c
                        "select + ffn launch"));
         return ok();
     }
+    if (T <= moe::kSmallRouteTokens && r->n_cold > 0 && !direct && moe::ffn_select_fusable(T, k, E, H, s->inter)) {
+        // one token with cold experts, all on the caller's stream: the hot
+        // experts' gate/up (its blocks select and publish the pick set), the
+        // gather (its own top-k), then the cold experts' gate/up and the down
+        // projection with the combine.  Measured against running the gather
+        // beside the hot gate/up on a second stream: that overlap slows the
+        // gate/up by more than it hides (per layer with nothing cold 50.7
+        // against 41.3 us; the 40-layer one-stream step 3.00 against 2.63 ms)
+        const moe::FfnArgs a = ffn_args(s, T, x, topk_ids, topk_w, out_dtype, out);
+        const int P = T * k;
+        TRY(hip_status(moe::launch_ffn_select_hot(a, z, renormalize != 0, topk_ids, topk_w, g, w, L, st),
+                       "hot ffn launch"));
+        TRY(hip_status(moe::launch_gather_sel(z, T, E, k, r->slot, r->n_cold, r->host_cold, r->scratch, g.blob_bytes,
+                                              st),
+                       "gather launch"));
+        TRY(hip_status(moe::launch_ffn_part(a, moe::kPartCold, r->n_cold < P ? r->n_cold : P, w, L, st),
+                       "cold ffn launch"));
+        return ok();
+    }
     if (T <= moe::kSmallRouteTokens && r->n_cold > 0 && !direct && moe::ffn_block_path(T, H, s->inter)) {
-        // decode with cold experts: the gather, forked right after the router,
-        // takes the top-k from the logits itself on the side stream, so it
-        // waits for no grouping; the hot experts' FFN runs meanwhile on the
-        // caller's stream (at one token its gate/up selects in every block
-        // and publishes the pick set, else one select-and-group launch comes
-        // first); the cold experts' FFN and the combine follow the join
+        // decode with cold experts, more tokens: the gather, forked right
+        // after the router, takes the top-k from the logits itself on the
+        // side stream, so it waits for no grouping; one select-and-group
+        // launch and the hot experts' FFN run meanwhile on the caller's
+        // stream; the cold experts' FFN and the combine follow the join
         const moe::FfnArgs a = ffn_args(s, T, x, topk_ids, topk_w, out_dtype, out);
         const int P = T * k;
         std::unique_lock<std::mutex> lock;
@@ -427,14 +445,9 @@ moe_status moe_layer_forward(const moe_shape *s, int32_t T, const uint16_t *x, c
                                               side->st),
                        "gather launch"));
         TRY(hip_status(hipEventRecord(side->join, side->st), "gather join"));
-        if (moe::ffn_select_fusable(T, k, E, H, s->inter)) {
-            TRY(hip_status(moe::launch_ffn_select_hot(a, z, renormalize != 0, topk_ids, topk_w, g, w, L, st),
-                           "hot ffn launch"));
-        } else {
-            TRY(hip_status(moe::launch_select_group_small(z, T, k, renormalize != 0, topk_ids, topk_w, g, w, L, st),
-                           "select-and-group launch"));
-            TRY(hip_status(moe::launch_ffn_part(a, moe::kPartHot, E < P ? E : P, w, L, st), "hot ffn launch"));
-        }
+        TRY(hip_status(moe::launch_select_group_small(z, T, k, renormalize != 0, topk_ids, topk_w, g, w, L, st),
+                       "select-and-group launch"));
+        TRY(hip_status(moe::launch_ffn_part(a, moe::kPartHot, E < P ? E : P, w, L, st), "hot ffn launch"));
         TRY(hip_status(hipStreamWaitEvent(st, side->join, 0), "gather join"));
         lock.unlock();
         TRY(hip_status(moe::launch_ffn_part(a, moe::kPartCold, r->n_cold < P ? r->n_cold : P, w, L, st),

@@ -92,9 +92,9 @@ constexpr int kFusedSelectPairs = 512;
 // Pairs up to which the layer uses the gate/up kernel that selects in every
 // block.  The per-block selection grows with T while the launch it saves
 // does not: measured per layer (4 layers rotating, graph replay), it wins at
-// one token (34 against 35.5 us all resident, 50.5 against 53 us hot/cold)
-// and loses from two tokens on (all resident: 58 against 54 us at T = 2, 155
-// against 111 at T = 8, 848 against 256 at T = 32).
+// one token (34 against 35.5 us all resident) and loses from two tokens on
+// (58 against 54 us at T = 2, 155 against 111 at T = 8, 848 against 256 at
+// T = 32).
 constexpr int kFusedSelectMaxPairs = 8;
 hipError_t launch_ffn_select(const FfnArgs &a, const float *z, int renorm, int32_t *ids, float *w,
                              const GroupArgs &g, char *ws, const WsLayout &L, hipStream_t st);
