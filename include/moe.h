@@ -192,11 +192,11 @@ moe_status moe_expert_ffn(const moe_shape *s, int32_t n_tokens, const uint16_t *
  * the combine, ordered
  * on `stream`: the call returns with everything enqueued after work already
  * on `stream` and later work on `stream` sees the finished layer.  At decode
- * sizes above one token (T*k > 8) with cold experts, the gather runs on a
+ * sizes above a few tokens (T*k > 24) with cold experts, the gather runs on a
  * library-owned side stream of the current device (default priority, created
  * on first use) forked from and joined back into `stream` by events, while
  * the hot experts' FFN runs on `stream`; the pattern is valid under stream
- * capture.  At one token everything runs on `stream`.  topk_ids / topk_w
+ * capture.  Below that everything runs on `stream`.  topk_ids / topk_w
  * receive the routing. */
 moe_status moe_layer_forward(const moe_shape *s, int32_t n_tokens, const uint16_t *x,
                              const float *w_router, const float *bias, int32_t renormalize,

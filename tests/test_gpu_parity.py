@@ -182,7 +182,8 @@ def boost_cold(L, delta):
     L.bias.copy_(torch.from_numpy(L.bias_np))
 
 
-@pytest.mark.parametrize("T,delta", [(32, 3.0), (5, 3.0), (32, 0.0), (1, 3.0), (1, 40.0), (8, 40.0)])
+@pytest.mark.parametrize("T,delta", [(32, 3.0), (5, 3.0), (32, 0.0), (1, 3.0), (1, 40.0), (8, 40.0),
+                                     (2, 3.0), (4, 3.0), (4, 40.0)])
 def test_decode_cold_picks_overlapped(T, delta):
     """Decode layer with many picked cold experts: the gather runs on the side
     stream while the hot experts' FFN runs; ids, gathered bytes and outputs
@@ -491,7 +492,7 @@ def test_gpu_error_paths():
 
 
 @pytest.mark.parametrize("name,T,delta", [("tiny", 8, 0.0), ("hotcold8", 8, 0.0), ("hotcold8", 32, 3.0),
-                                          ("hotcold8", 1, 3.0), ("hotcold8", 1, 0.0)])
+                                          ("hotcold8", 1, 3.0), ("hotcold8", 1, 0.0), ("hotcold8", 4, 3.0)])
 def test_graph_replay_matches_eager(name, T, delta):
     """The layer captured in a HIP graph gives the eager result on every
     replay, with eager work and synchronisations between replays (with cold
