@@ -416,17 +416,17 @@ moe_status moe_layer_forward(const moe_shape *s, int32_t T, const uint16_t *x, c
     if (T <= moe::kSmallRouteTokens && r->n_cold > 0 && !direct && moe::ffn_select_fusable(T, k, E, H, s->inter)) {
         // one token with cold experts, all on the caller's stream: the hot
         // experts' gate/up (its blocks select and publish the pick set), the
-        // gather (its own top-k), then the cold experts' gate/up and the down
-        // projection with the combine.  Measured against running the gather
-        // beside the hot gate/up on a second stream: that overlap slows the
-        // gate/up by more than it hides (per layer with nothing cold 50.7
-        // against 41.3 us; the 40-layer one-stream step 3.00 against 2.63 ms)
+        // gather of the published cold list, then the cold experts' gate/up
+        // and the down projection with the combine.  Measured against running
+        // a self-selecting gather beside the hot gate/up on a second stream:
+        // that overlap slows the gate/up by more than it hides (per layer
+        // with nothing cold 50.7 against 37.7 us; the 40-layer one-stream
+        // step 3.00 against 2.48 ms)
         const moe::FfnArgs a = ffn_args(s, T, x, topk_ids, topk_w, out_dtype, out);
         const int P = T * k;
         TRY(hip_status(moe::launch_ffn_select_hot(a, z, renormalize != 0, topk_ids, topk_w, g, w, L, st),
                        "hot ffn launch"));
-        TRY(hip_status(moe::launch_gather_sel(z, T, E, k, r->slot, r->n_cold, r->host_cold, r->scratch, g.blob_bytes,
-                                              st),
+        TRY(hip_status(moe::launch_gather(r->host_cold, r->scratch, g.blob_bytes, r->slot, w, L, st),
                        "gather launch"));
         TRY(hip_status(moe::launch_ffn_part(a, moe::kPartCold, r->n_cold < P ? r->n_cold : P, w, L, st),
                        "cold ffn launch"));
@@ -435,17 +435,17 @@ moe_status moe_layer_forward(const moe_shape *s, int32_t T, const uint16_t *x, c
     if (T <= moe::kSmallRouteTokens && r->n_cold > 0 && !direct && moe::ffn_block_path(T, H, s->inter) &&
         T * k <= kGatherOverlapMinPairs) {
         // a few tokens with cold experts, in order on the caller's stream:
-        // select and group, the hot experts' FFN, the gather (its own top-k),
-        // the cold experts' FFN and the combine.  Measured per layer against
-        // the side-stream overlap below: 64 against 75 us at 2 tokens, 88
-        // against 98 at 4; the overlap wins from 8 tokens on (173 against 189)
+        // select and group, the hot experts' FFN, the gather of the published
+        // cold list, the cold experts' FFN and the combine.  Measured per
+        // layer against the side-stream overlap below: 59 against 75 us at 2
+        // tokens, 83 against 98 at 4; the overlap wins from 8 tokens on (173
+        // against 189)
         const moe::FfnArgs a = ffn_args(s, T, x, topk_ids, topk_w, out_dtype, out);
         const int P = T * k;
         TRY(hip_status(moe::launch_select_group_small(z, T, k, renormalize != 0, topk_ids, topk_w, g, w, L, st),
                        "select-and-group launch"));
         TRY(hip_status(moe::launch_ffn_part(a, moe::kPartHot, E < P ? E : P, w, L, st), "hot ffn launch"));
-        TRY(hip_status(moe::launch_gather_sel(z, T, E, k, r->slot, r->n_cold, r->host_cold, r->scratch, g.blob_bytes,
-                                              st),
+        TRY(hip_status(moe::launch_gather(r->host_cold, r->scratch, g.blob_bytes, r->slot, w, L, st),
                        "gather launch"));
         TRY(hip_status(moe::launch_ffn_part(a, moe::kPartCold, r->n_cold < P ? r->n_cold : P, w, L, st),
                        "cold ffn launch"));
