@@ -119,10 +119,14 @@ __device__ __forceinline__ int block_exscan1024(int v, int *lds, int *tot) {
 
 constexpr int kPerLane = kMaxExperts / kWave;
 
-// Order-preserving map of a float to uint32 (larger float -> larger key); NaN
-// maps like -inf.  key_to_float inverts it.
+// Order-preserving map of a float to uint32 (larger float -> larger key).
+// -0 and +0 get one key (they compare equal, so they tie and the lower
+// index goes first); NaN gets key 1, below every number including -inf
+// (key 0x007fffff), so a NaN logit is picked last, after -inf.
+// key_to_float inverts it (+0 for both zeros, a NaN for key 1).
 __device__ __forceinline__ uint32_t float_key(float v) {
-    const uint32_t u = (v == v) ? __float_as_uint(v) : 0xff800000u;
+    if (v != v) return 1u;
+    const uint32_t u = (v == 0.0f) ? 0u : __float_as_uint(v);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 __device__ __forceinline__ float key_to_float(uint32_t k) {
@@ -157,10 +161,11 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t key) {
 
 // Top-k of one token's E logits by one wave (NPL >= E / 64 values per lane).
 // Each logit becomes the 64-bit key (float_key(z), E - 1 - e), so the key
-// order is: larger logit first, equal logits by lower expert index; NaN
-// orders as -inf.  k rounds take the wave maximum and clear it (key 0 is
-// below every real key).  Pick j (k <= 32) ends in lane j, which returns its
-// expert and softmax weight (renormalised over the k picks, or over all E).
+// order is: larger logit first, equal logits (+0 and -0 included) by lower
+// expert index, NaN after -inf.  k rounds take the wave maximum and clear it
+// (key 0 is below every real key; a NaN's is (1, .) > 0).  Pick j (k <= 32)
+// ends in lane j, which returns its expert and softmax weight (renormalised
+// over the k picks, or over all E; a picked NaN logit gives a NaN weight).
 template <int NPL>
 __device__ __forceinline__ void topk_wave(const float *__restrict__ zr, int E, int k, int renorm, int *pick_e,
                                           float *pick_w) {
@@ -175,8 +180,8 @@ __device__ __forceinline__ void topk_wave(const float *__restrict__ zr, int E, i
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
         const int e = lane + 64 * i;
-        v[i] = (e < E && v[i] == v[i]) ? v[i] : -INFINITY;
         key[i] = e < E ? (((uint64_t)float_key(v[i]) << 32) | (uint32_t)(E - 1 - e)) : 0;
+        v[i] = (e < E && v[i] == v[i]) ? v[i] : -INFINITY;   // the all-E softmax sum skips NaN
     }
     uint64_t mine = 0;
     for (int j = 0; j < k; ++j) {

@@ -112,3 +112,20 @@ def test_selection_on_fp32_logits_is_exact():
 def test_margin():
     z = np.array([[3.0, 1.0, 2.0, 0.5]])
     assert route.topk_margin(z, 2)[0] == 1.0
+
+
+def test_signed_zeros_tie_to_lower_index():
+    """+0 and -0 compare equal, so they tie like any equal logits."""
+    z = np.array([[-1.0, -0.0, 0.0, -2.0],
+                  [-1.0, 0.0, -0.0, -2.0]])
+    assert route.select_topk(z, 1).tolist() == [[1], [1]]
+    assert route.select_topk(z, 2).tolist() == [[1, 2], [1, 2]]
+
+
+def test_nan_logits_rank_after_minus_infinity():
+    """Reading taken: a NaN logit ranks below every number (-inf included),
+    NaNs among themselves by increasing index."""
+    nan, inf = float("nan"), float("inf")
+    z = np.array([[nan, -inf, 1.0, nan, -inf, 0.5]])
+    assert route.select_topk(z, 6).tolist() == [[2, 5, 1, 4, 0, 3]]
+    assert route.select_topk(z, 3).tolist() == [[2, 5, 1]]
