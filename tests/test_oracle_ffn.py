@@ -159,3 +159,14 @@ def test_silu_large_negative_is_signed_zero():
     h = ffn.silu(np.array([-1e4, 0.0, 1e4], dtype=np.float32))
     assert h[0] == 0 and math.copysign(1, h[0]) == -1
     assert h[1] == 0 and h[2] == 1e4
+
+
+def test_layer_experts_on_threads_give_the_same_bits():
+    """The thread-pool evaluation used by the full-size GPU tests changes only
+    the order in which independent experts are evaluated."""
+    from tests import oracle_threads
+    x, wr, blobs = _inputs(3)
+    a = layer.layer_forward(x, wr, None, lambda e: blobs[e], H, I, K)
+    b = oracle_threads.layer_forward(x, wr, None, lambda e: blobs[e], H, I, K)
+    assert np.array_equal(a["ids"], b["ids"])
+    assert np.array_equal(a["out"], b["out"])
