@@ -119,9 +119,20 @@ class Workload:
         self.layer.close()
 
 
-def time_steps(w: Workload, steps: int, warmup: int, use_graph: bool):
-    """Wall time of about `steps` whole-layer steps (rounded up to whole
-    replays of the pool); returns (seconds, steps timed, graph used)."""
+REPEATS = 3          # timed repeats of the K steps; the figure is their median
+AGREE = 0.02         # repeats agree when (max - min) / median is within 2%
+
+
+def spread(xs) -> float:
+    xs = sorted(xs)
+    return (xs[-1] - xs[0]) / xs[len(xs) // 2]
+
+
+def time_steps(w: Workload, steps: int, warmup: int, use_graph: bool, repeats: int = REPEATS):
+    """Seconds of exactly `steps` whole-layer steps (step i runs batch i mod
+    the pool size), timed `repeats` times after `warmup` untimed eager steps.
+    With a graph, the K steps are captured once (one untimed replay) and each
+    repeat is one replay.  Returns (list of seconds per repeat, graph used)."""
     import torch
     for i in range(warmup):
         w.step(i)
@@ -133,7 +144,7 @@ def time_steps(w: Workload, steps: int, warmup: int, use_graph: bool):
             s.wait_stream(torch.cuda.current_stream())
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph, stream=s, capture_error_mode="relaxed"):
-                for i in range(w.reps):
+                for i in range(steps):
                     w.step(i, stream=s)
             torch.cuda.synchronize()
             graph.replay()
@@ -142,37 +153,46 @@ def time_steps(w: Workload, steps: int, warmup: int, use_graph: bool):
             log(f"graph capture failed ({e}); timing eager launches")
             graph = None
             torch.cuda.synchronize()
-    if graph is not None:
-        n_rep = max(1, -(-steps // w.reps))
-        steps = n_rep * w.reps
+    graphed = graph is not None
+    secs = []
+    for _ in range(repeats):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(n_rep):
+        if graph is not None:
             graph.replay()
+        else:
+            for i in range(steps):
+                w.step(i)
         torch.cuda.synchronize()
-        return time.perf_counter() - t0, steps, True
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        w.step(i)
-    torch.cuda.synchronize()
-    return time.perf_counter() - t0, steps, False
+        secs.append(time.perf_counter() - t0)
+    del graph
+    return secs, graphed
 
 
-def profile_kernels(w: Workload, steps: int) -> dict:
-    """Per-kernel (launches, mean microseconds) from the library's HIP events."""
+def profile_kernels(w: Workload, steps: int, repeats: int = REPEATS):
+    """Per-kernel (launches per pass, median over `repeats` passes of the mean
+    microseconds) from the library's HIP events, over eager passes of
+    `steps` steps; and per kernel the spread of those means."""
     import torch
     import moe_routed_expert_router_amd as moe
-    torch.cuda.synchronize()
-    moe.moe_profile_reset()
-    moe.moe_profile_enable(True)
-    for i in range(steps):
-        w.step(i)
-    torch.cuda.synchronize()
-    moe.moe_profile_enable(False)
-    stats = moe.moe_profile_read()
-    moe.moe_profile_reset()
-    return {k: (n, 1e3 * ms / n) for k, (n, ms) in stats.items() if n}
+    runs = []
+    for _ in range(repeats):
+        torch.cuda.synchronize()
+        moe.moe_profile_reset()
+        moe.moe_profile_enable(True)
+        for i in range(steps):
+            w.step(i)
+        torch.cuda.synchronize()
+        moe.moe_profile_enable(False)
+        stats = moe.moe_profile_read()
+        moe.moe_profile_reset()
+        runs.append({k: (n, 1e3 * ms / n) for k, (n, ms) in stats.items() if n})
+    prof, spreads = {}, {}
+    for k in runs[0]:
+        us = [r[k][1] for r in runs if k in r]
+        prof[k] = (runs[0][k][0], float(np.median(us)))
+        spreads[k] = spread(us)
+    return prof, spreads
 
 
 def ffn_bytes(w: Workload, picks_per_step: list[np.ndarray]) -> dict:
@@ -253,11 +273,27 @@ def cpu_baseline(name: str, seconds: float) -> dict:
     workload at a time, until about `seconds` of CPU work have run."""
     from synth import gen
     from oracle import layer as olayer
+    blas = []
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        blas = [{"api": i.get("internal_api"), "threads": i.get("num_threads"), "version": i.get("version")}
+                for i in info]
     except Exception:
         threads = os.cpu_count() or 1
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
+    cpu_model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     wl = gen.workload(name)
     cal = gen.load_calibration() if wl.zipf else None
     bias = gen.zipf_prior(wl.seed, 0, wl.n_experts, cal["alpha"]) if wl.zipf else None
@@ -278,23 +314,163 @@ def cpu_baseline(name: str, seconds: float) -> dict:
     return {"value": n_tok / elapsed, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{batches} batches of {wl.tokens} token(s) of the {name} layer (seed {wl.seed}), "
                       f"{elapsed:.1f} s of oracle time (route, dequant, fp32 SwiGLU FFN, combine)",
-            "host_cpus": os.cpu_count()}
+            "host_cpus": os.cpu_count(), "affinity_cpus": affinity, "cpu_model": cpu_model, "blas": blas}
 
 
 def measure(name: str, steps: int, warmup: int, reps: int, use_graph: bool, prof_steps: int):
+    """Timed steps (time_steps) and kernel profile (profile_kernels) of one
+    workload; returns (workload, seconds per repeat, graph used, profile,
+    profile spreads, algorithmic bytes)."""
     import torch
-    w = Workload(name, reps)
+    w = Workload(name, min(reps, steps))
     try:
-        secs, steps_done, graphed = time_steps(w, steps, warmup, use_graph)
-        # picks of the pool (the graph replays exactly these batches)
+        secs, graphed = time_steps(w, steps, warmup, use_graph)
+        # picks of the pool (the timed steps ran exactly these batches)
         torch.cuda.synchronize()
         picks = [t.cpu().numpy() for t in w.ids]
-        prof = profile_kernels(w, prof_steps)
+        prof, pspread = profile_kernels(w, prof_steps)
         by = ffn_bytes(w, picks)
-        return w, secs, steps_done, graphed, prof, by
+        return w, secs, graphed, prof, pspread, by
     except Exception:
         w.close()
         raise
+
+
+def layer_figures(name: str, steps: int, warmup: int, reps: int, use_graph: bool) -> dict:
+    """Whole-layer figures of one workload: tokens/s (median of the timed
+    repeats of exactly `steps` steps, with their spread), per-kernel times,
+    the dominant kernel's roofline and the grouped FFN's HBM rate."""
+    import torch
+    w, secs, graphed, prof, pspread, by = measure(name, steps, warmup, reps, use_graph, min(steps, 256))
+    try:
+        wl = w.wl
+        med = float(np.median(secs))
+        rep = {"n": len(secs), "seconds": [round(x, 6) for x in secs], "spread": round(spread(secs), 4),
+               "agree_within_2pct": spread(secs) <= AGREE}
+        log(f"[bench] {name}: {steps} steps x {len(secs)} repeats, median {med:.4f} s "
+            f"({1e6 * med / steps:.1f} us/step, spread {100 * spread(secs):.2f}%), graph={graphed}")
+        kernels = kernel_table(prof, by)
+        for k, e in kernels.items():
+            if k in pspread:
+                e["spread"] = round(pspread[k], 4)
+            log(f"[bench]   {k:24s} {e['us_per_forward']:9.2f} us/forward" +
+                (f"  {e['GB_per_s']:8.1f} GB/s" if "GB_per_s" in e else ""))
+        dom = role_kernel(prof, "gate_up")
+        dn = role_kernel(prof, "down")
+        dom_us = prof[dom][1]
+        achieved = by["gate_up"] / (dom_us * 1e-6) / 1e9
+        ffn_us = role_us(prof, "gate_up") + role_us(prof, "down") + role_us(prof, "combine")
+        ffn_gbs = (by["gate_up"] + by["down"]) / (ffn_us * 1e-6) / 1e9
+        if wl.tokens > 32:
+            # prefill: the grouped GEMM is a dense contraction; its bound is
+            # the bf16 matrix-core peak.  Algorithmic flops of gate/up: 2*P*H*2I.
+            flops = 2.0 * wl.tokens * wl.top_k * wl.hidden * 2 * wl.inter
+            tf = flops / (dom_us * 1e-6) / 1e12
+            roofline = {"bound": "mfma", "kernel": dom, "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFS,
+                        "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
+                        "flops_per_launch": flops, "mean_launch_us": round(dom_us, 3),
+                        "spread": round(pspread[dom], 4), "hbm_GB_per_s": round(achieved, 1)}
+            dflops = 2.0 * wl.tokens * wl.top_k * wl.inter * wl.hidden
+            layer_flops = flops + dflops + 2.0 * wl.tokens * wl.n_experts * wl.hidden
+            extra = {"down_kernel": dn, "down_TFLOP_per_s": round(dflops / (prof[dn][1] * 1e-6) / 1e12, 1),
+                     "layer_useful_TFLOP_per_s": round(layer_flops * steps / med / 1e12, 1)}
+        else:
+            roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                        "traffic": read_traffic(dom, name), "bytes_per_launch": int(by["gate_up"]),
+                        "mean_launch_us": round(dom_us, 3), "spread": round(pspread[dom], 4)}
+            extra = {}
+        out = {"tokens_per_s": round(steps * wl.tokens / med, 2), "ms_per_step": round(1e3 * med / steps, 5),
+               "steps": steps, "repeats": rep, "graph": graphed, "mean_distinct_experts": round(by["unique"], 2),
+               "roofline": roofline,
+               "ffn": {"kernels": [dom, dn], "us": round(ffn_us, 3), "hbm_GB_per_s": round(ffn_gbs, 1),
+                       "frac": round(ffn_gbs / HBM_PEAK_GBS, 4)},
+               "kernels": kernels, "_wl": wl}
+        out.update(extra)
+        if "gather_cold" in prof and by["gather_cold"] > 0:
+            out["gather_link_GB_per_s"] = round(by["gather_cold"] / (role_us(prof, "gather_cold") * 1e-6) / 1e9, 2)
+            out["gather_bytes_per_step"] = int(by["gather_cold"])
+        return out
+    finally:
+        w.close()
+        del w
+        torch.cuda.empty_cache()
+
+
+def measure_read_ceiling(sizes=(26886144, 53534720, 80420864), launches: int = 24) -> dict:
+    """The single-launch streaming-read ceiling: moe_probe_read over fresh
+    bytes at each size (the decode1 down, gate/up and whole-FFN volumes),
+    launches rotating over a pool larger than the Infinity Cache, kernel time
+    from the library's launch events; the best of 4, 8 and 16 loads per
+    thread, with the median of the launches."""
+    import torch
+    import moe_routed_expert_router_amd as moe
+    pool_bytes = max(1 << 30, 12 * max(sizes))
+    pool = torch.empty(pool_bytes, dtype=torch.uint8, device="cuda")
+    pool.fill_(0x5A)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = {}
+    try:
+        for n in sizes:
+            n16 = n // 16 * 16
+            slots = pool_bytes // n16
+            best = None
+            for lpt in (4, 8, 16):
+                for i in range(4):   # untimed
+                    moe.moe_probe_read(pool[(i % slots) * n16:], n16, lpt, sink)
+                torch.cuda.synchronize()
+                us = []
+                for i in range(launches):
+                    moe.moe_profile_reset()
+                    moe.moe_profile_enable(True)
+                    moe.moe_probe_read(pool[(i % slots) * n16:], n16, lpt, sink)
+                    torch.cuda.synchronize()
+                    moe.moe_profile_enable(False)
+                    cnt, ms = moe.moe_profile_read()["probe_read"]
+                    us.append(1e3 * ms / cnt)
+                med = float(np.median(us))
+                if best is None or med < best[1]:
+                    best = (lpt, med, spread(us))
+            lpt, med, sp = best
+            gbs = n16 / (med * 1e-6) / 1e9
+            out[f"{n16 / 1e6:.1f}MB"] = {"bytes": n16, "loads_per_thread": lpt, "kernel_us": round(med, 3),
+                                         "GB_per_s": round(gbs, 1), "frac_of_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                                         "spread": round(sp, 4)}
+            log(f"[bench] read ceiling {n16 / 1e6:6.1f} MB: {med:7.2f} us = {gbs:7.1f} GB/s "
+                f"({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s), {lpt} loads/thread")
+        return out
+    finally:
+        moe.moe_profile_reset()
+        del pool
+        torch.cuda.empty_cache()
+
+
+def measure_host_call(name: str = "decode1", calls: int = 200) -> dict:
+    """Host time of one eager moe_layer_forward call (argument checks,
+    pointer lookups and launches; the call does not wait for the GPU)."""
+    import torch
+    import moe_routed_expert_router_amd as moe
+    from synth import gen
+    from tests.gpu_setup import Layer
+    L = Layer(gen.workload(name))
+    try:
+        for _ in range(10):
+            L.forward()
+        torch.cuda.synchronize()
+        st = torch.cuda.current_stream().cuda_stream
+        t = []
+        for i in range(calls):
+            t0 = time.perf_counter()
+            moe.moe_layer_forward(L.shape, L.x, L.wr, L.bias, True, L.residency, L.ids, L.w, L.out, L.ws, st)
+            t.append(time.perf_counter() - t0)
+            if i % 16 == 15:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        us = 1e6 * np.array(t)
+        return {"workload": name, "calls": calls, "median_us": round(float(np.median(us)), 2),
+                "p90_us": round(float(np.percentile(us, 90)), 2)}
+    finally:
+        L.close()
 
 
 def measure_ffn_batches(batches=(1, 8, 32), layers: int = 4, reps: int = 10) -> dict:
@@ -315,7 +491,8 @@ def measure_ffn_batches(batches=(1, 8, 32), layers: int = 4, reps: int = 10) -> 
                 L.forward()
             torch.cuda.synchronize()
             picks = [(L, L.ids.cpu().numpy()) for L in Ls]
-            for it in range(2):   # one untimed round, then the profiled one
+            runs = []
+            for it in range(1 + REPEATS):   # one untimed round, then the profiled ones
                 if it:
                     moe.moe_profile_reset()
                     moe.moe_profile_enable(True)
@@ -323,13 +500,16 @@ def measure_ffn_batches(batches=(1, 8, 32), layers: int = 4, reps: int = 10) -> 
                     for L in Ls:
                         moe.moe_expert_ffn(L.shape, L.x, L.ids, L.w, L.residency, L.out, L.ws)
                 torch.cuda.synchronize()
-            moe.moe_profile_enable(False)
-            raw = moe.moe_profile_read()
-            moe.moe_profile_reset()
-            prof = {k: (n, 1e3 * ms / n) for k, (n, ms) in raw.items() if n}
-            per = layers * reps
-            us = {r: sum(n * u for k, (n, u) in prof.items() if kernel_role(k) == r) / per
-                  for r in ("gate_up", "down", "combine")}
+                if it:
+                    moe.moe_profile_enable(False)
+                    raw = moe.moe_profile_read()
+                    moe.moe_profile_reset()
+                    prof = {k: (n, 1e3 * ms / n) for k, (n, ms) in raw.items() if n}
+                    per = layers * reps
+                    runs.append({r: sum(n * u for k, (n, u) in prof.items() if kernel_role(k) == r) / per
+                                 for r in ("gate_up", "down", "combine")})
+            us = {r: float(np.median([x[r] for x in runs])) for r in ("gate_up", "down", "combine")}
+            ffn_runs = [x["gate_up"] + x["down"] + x["combine"] for x in runs]
             by = layer_bytes(picks)
             ffn_us = us["gate_up"] + us["down"] + us["combine"]
             gbs = (by["gate_up"] + by["down"]) / (ffn_us * 1e-6) / 1e9
@@ -339,7 +519,8 @@ def measure_ffn_batches(batches=(1, 8, 32), layers: int = 4, reps: int = 10) -> 
                 "combine_us": round(us["combine"], 3),
                 "gate_up_GB_per_s": round(by["gate_up"] / (us["gate_up"] * 1e-6) / 1e9, 1),
                 "down_GB_per_s": round(by["down"] / (us["down"] * 1e-6) / 1e9, 1),
-                "ffn_hbm_GB_per_s": round(gbs, 1), "ffn_frac": round(gbs / HBM_PEAK_GBS, 4)}
+                "ffn_hbm_GB_per_s": round(gbs, 1), "ffn_frac": round(gbs / HBM_PEAK_GBS, 4),
+                "ffn_us_spread": round(spread(ffn_runs), 4)}
             log(f"[bench] ffn batch {T}: {ffn_us:.1f} us, {gbs:.0f} GB/s")
         finally:
             for L in Ls:
@@ -710,7 +891,10 @@ def measure_layer_copy(T: int = 32, layers: int = 40, reps: int = 3) -> dict:
     experts, 5.13 GB, kept in pinned host memory as a layer offloader keeps
     it) copied to HBM before the layer runs, then the layer computed on the
     copy.  The copy is timed two ways: the gather kernel with every expert
-    picked, and the DMA engines (a plain host -> device tensor copy).  Per-
+    picked, and the DMA engines (the host pool copied into the same HBM area
+    by hipMemcpyAsync); after each, all 384 copied blobs are compared with
+    the host bytes.  The forward then runs with the copy as the layer's HBM
+    pool and its output is compared with the same layer fully resident.  Per-
     step tokens/s is for `layers` such layers at T tokens each, to set
     beside the picked-only step of the same shape."""
     import torch
@@ -739,27 +923,45 @@ def measure_layer_copy(T: int = 32, layers: int = 40, reps: int = 3) -> dict:
             torch.cuda.synchronize()
             return t0.elapsed_time(t1) / reps
 
-        kern_ms = timed(lambda: moe.moe_gather_cold(L.shape, ids, L.residency, ws))
-        same = bool(np.array_equal(L.scratch[:4].cpu().numpy().ravel(), L.host.np[:4 * B]))
-        src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+        host_dev = torch.from_numpy(L.host.np).cuda()   # the host bytes, for the comparisons
         dst = L.scratch.view(-1)
+        dst.fill_(0)
+        kern_ms = timed(lambda: moe.moe_gather_cold(L.shape, ids, L.residency, ws))
+        gather_exact = bool(torch.equal(dst, host_dev))
+        src = torch.from_numpy(L.host.np)              # the pinned pool itself
+        assert src.is_pinned()
+        dst.fill_(0)
         dma_ms = timed(lambda: dst.copy_(src, non_blocking=True))
-        del src
-        hot = Layer(wl, T=T, all_hot=True)   # the layer computed on its HBM copy
+        dma_exact = bool(torch.equal(dst, host_dev))
+        del host_dev
+        # the layer on its copy: expert e sits in row e of the copied area
+        slot = torch.arange(E, dtype=torch.int32, device="cuda")
+        r = moe.residency(slot, L.scratch, None, None, E, 0)
+        out = torch.empty_like(L.out)
+
+        def fwd():
+            moe.moe_layer_forward(L.shape, L.x, L.wr, L.bias, True, r, L.ids, L.w, out, L.ws)
+
+        fwd_ms = timed(fwd)
+        ref = Layer(wl, T=T, all_hot=True)
         try:
-            fwd_ms = timed(lambda: hot.forward())
+            b = ref.forward()
+            torch.cuda.synchronize()
+            same_out = bool(torch.equal(out, b)) and bool(torch.equal(L.ids, ref.ids))
         finally:
-            hot.close()
+            ref.close()
         copy_ms = min(kern_ms, dma_ms)
         step_ms = layers * (copy_ms + fwd_ms)
         res = {"bytes_per_layer": nbytes, "experts": E,
                "gather_kernel_ms": round(kern_ms, 3), "gather_kernel_GB_per_s": round(nbytes / kern_ms / 1e6, 2),
                "dma_copy_ms": round(dma_ms, 3), "dma_copy_GB_per_s": round(nbytes / dma_ms / 1e6, 2),
-               "forward_resident_ms": round(fwd_ms, 4), "tokens_per_layer": T, "layers": layers,
+               "forward_on_copy_ms": round(fwd_ms, 4), "tokens_per_layer": T, "layers": layers,
                "ms_per_step": round(step_ms, 2), "tokens_per_s": round(T / (step_ms * 1e-3), 2),
-               "gather_copy_bit_exact": same}
+               "gather_copy_bit_exact": gather_exact, "dma_copy_bit_exact": dma_exact,
+               "blobs_compared": E, "forward_on_copy_equals_resident": same_out}
         log(f"[bench] layer copy: {nbytes / 1e9:.2f} GB per layer, kernel {kern_ms:.1f} ms "
             f"({nbytes / kern_ms / 1e6:.1f} GB/s), DMA {dma_ms:.1f} ms ({nbytes / dma_ms / 1e6:.1f} GB/s); "
+            f"forward on the copy {fwd_ms:.3f} ms (= resident: {same_out}); "
             f"{layers} layers x {T} tokens: {res['tokens_per_s']} tok/s")
         return res
     finally:
@@ -872,15 +1074,18 @@ def measure_stack(name: str, steps: int, warmup: int, use_graph: bool, one_token
             except Exception as e:
                 log(f"[bench] {name}: graph capture failed ({e}); timing eager steps")
                 graph = None
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            if graph is not None:
-                graph.replay()
-            else:
-                S.forward()
-        torch.cuda.synchronize()
-        secs = time.perf_counter() - t0
+        reps = []
+        for _ in range(REPEATS):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                if graph is not None:
+                    graph.replay()
+                else:
+                    S.forward()
+            torch.cuda.synchronize()
+            reps.append(time.perf_counter() - t0)
+        secs = float(np.median(reps))
         picks = [(L, L.ids.cpu().numpy()) for L in S.layers]
         moe.moe_profile_reset()
         moe.moe_profile_enable(True)
@@ -895,6 +1100,8 @@ def measure_stack(name: str, steps: int, warmup: int, use_graph: bool, one_token
         ffn_us = role_us(prof, "gate_up") + role_us(prof, "down") + role_us(prof, "combine")
         entry = {"tokens_per_s": round(steps * wl.tokens / secs, 2), "ms_per_step": round(1e3 * secs / steps, 4),
                  "layers": wl.layers, "tokens_per_layer": wl.tokens, "steps": steps, "graph": graph is not None,
+                 "repeats": {"n": len(reps), "seconds": [round(x, 5) for x in reps], "spread": round(spread(reps), 4),
+                             "agree_within_2pct": spread(reps) <= AGREE},
                  "distinct_cold_pools": S.distinct_host_pools,
                  "mean_distinct_experts_per_layer": round(by["unique"], 2),
                  "ffn_hbm_GB_per_s": round((by["gate_up"] + by["down"]) / (ffn_us * 1e-6) / 1e9, 1),
@@ -934,13 +1141,15 @@ def main():
     ap.add_argument("--no-ffn-batches", action="store_true",
                     help="skip the standalone grouped-FFN figures at batch 1/8/32")
     ap.add_argument("--no-step40", action="store_true", help="skip the 40-layer batch-32 secondary figures")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-layer secondary figures")
+    ap.add_argument("--no-read-ceiling", action="store_true", help="skip the streaming-read ceiling probe")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="first run one plain float64 copy of this many MiB (a known-size kernel for "
                          "scaling hardware byte counters)")
     a = ap.parse_args()
     if a.primary_only:
         for k in ("no_batch8", "no_adaptive", "no_verify", "no_layer_copy", "no_direct_read", "no_ffn_batches",
-                  "no_step40", "no_gather_sweep"):
+                  "no_step40", "no_gather_sweep", "no_prefill", "no_read_ceiling"):
             setattr(a, k, True)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -979,38 +1188,8 @@ def main():
                           "step40_batch32": e}), flush=True)
         return
     log(f"[bench] workload {a.workload}: setup")
-    w, secs, steps, graphed, prof, by = measure(a.workload, a.steps, a.warmup, a.reps, not a.no_graph,
-                                                min(a.steps, 256))
-    wl = w.wl
-    ms_per_step = 1e3 * secs / steps
-    value = steps * wl.tokens / secs
-    log(f"[bench] {steps} steps in {secs:.4f} s ({ms_per_step * 1e3:.1f} us/step), graph={graphed}")
-    kernels = kernel_table(prof, by)
-    for k, e in kernels.items():
-        log(f"[bench]   {k:24s} {e['us_per_forward']:9.2f} us/forward" +
-            (f"  {e['GB_per_s']:8.1f} GB/s" if "GB_per_s" in e else ""))
-    dom = role_kernel(prof, "gate_up")
-    dn = role_kernel(prof, "down")
-    dom_us = prof[dom][1]
-    achieved = by["gate_up"] / (dom_us * 1e-6) / 1e9
-    traffic = read_traffic(dom, a.workload)
-    ffn_us = role_us(prof, "gate_up") + role_us(prof, "down") + role_us(prof, "combine")
-    ffn_gbs = (by["gate_up"] + by["down"]) / (ffn_us * 1e-6) / 1e9
-    if wl.tokens > 32:
-        # prefill: the grouped GEMM is a dense contraction; its bound is the
-        # bf16 matrix-core peak.  Algorithmic flops of gate/up: 2*P*H*2I.
-        flops = 2.0 * wl.tokens * wl.top_k * wl.hidden * 2 * wl.inter
-        tf = flops / (dom_us * 1e-6) / 1e12
-        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFS,
-                    "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
-                    "flops_per_launch": flops, "mean_launch_us": round(dom_us, 3),
-                    "hbm_GB_per_s": round(achieved, 1)}
-    else:
-        roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                    "bytes_per_launch": int(by["gate_up"]), "mean_launch_us": round(dom_us, 3)}
-    w.close()
-    del w
+    prim = layer_figures(a.workload, a.steps, a.warmup, a.reps, not a.no_graph)
+    wl = prim.pop("_wl")
     torch.cuda.empty_cache()
 
     extra = {}
@@ -1028,24 +1207,23 @@ def main():
             torch.cuda.empty_cache()
 
     def batch8():
-        w8, s8, st8, g8, p8, b8 = measure("hotcold8", 128, 8, 16, not a.no_graph, 64)
-        try:
-            k8 = kernel_table(p8, b8)
-            ffn8_us = role_us(p8, "gate_up") + role_us(p8, "down") + role_us(p8, "combine")
-            entry = {"tokens_per_s": round(st8 * 8 / s8, 1), "ms_per_step": round(1e3 * s8 / st8, 4),
-                     "graph": g8, "mean_distinct_experts": round(b8["unique"], 2),
-                     "ffn_hbm_GB_per_s": round((b8["gate_up"] + b8["down"]) / (ffn8_us * 1e-6) / 1e9, 1),
-                     "kernels": k8}
-            if "gather_cold" in p8 and b8["gather_cold"] > 0:
-                entry["gather_link_GB_per_s"] = round(b8["gather_cold"] / (role_us(p8, "gather_cold") * 1e-6) / 1e9,
-                                                      2)
-                entry["gather_bytes_per_step"] = int(b8["gather_cold"])
-            return entry
-        finally:
-            w8.close()
-            torch.cuda.empty_cache()
+        f = layer_figures("hotcold8", 128, 8, 16, not a.no_graph)
+        f.pop("_wl")
+        return f
+
+    def prefill():
+        f = layer_figures("prefill8k", 20, 2, 2, not a.no_graph)
+        f.pop("_wl")
+        return f
 
     if a.workload == "decode1":
+        if not a.no_read_ceiling:
+            secondary("read_ceiling", "single-launch streaming-read ceiling (26.9 / 53.5 / 80.4 MB)",
+                      measure_read_ceiling)
+        if not a.no_prefill:
+            secondary("prefill8k", "prefill layer (8192 tokens, all resident, grouped GEMM)", prefill)
+        if not a.primary_only:
+            secondary("host_call", "host time of one eager moe_layer_forward (decode1)", measure_host_call)
         if not a.no_batch8:
             secondary("batch8_hotcold", "hotcold8 (batch 8, 255 hot / 129 cold)", batch8)
         if not a.no_direct_read:
@@ -1080,12 +1258,12 @@ def main():
 
     out = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": prim["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": steps,
+        "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": prim["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -1094,14 +1272,17 @@ def main():
         "config": {"workload": a.workload, "hidden": wl.hidden, "inter": wl.inter, "n_experts": wl.n_experts,
                    "top_k": wl.top_k, "tokens_per_step": wl.tokens, "layers": 1,
                    "resident": "all experts in HBM" if wl.n_hot is None else f"{wl.n_hot} hot / {wl.n_cold} cold",
-                   "weights": "MXFP4 (e2m1 + e8m0/32)", "accumulate": "fp32", "graph": graphed,
-                   "token_batches_rotated": a.reps},
-        "roofline": roofline,
-        "ffn": {"kernels": [dom, dn], "us": round(ffn_us, 3), "hbm_GB_per_s": round(ffn_gbs, 1),
-                "frac": round(ffn_gbs / HBM_PEAK_GBS, 4)},
-        "kernels": kernels,
+                   "weights": "MXFP4 (e2m1 + e8m0/32)", "accumulate": "fp32", "graph": prim["graph"],
+                   "token_batches_rotated": min(a.reps, a.steps)},
+        "repeats": prim["repeats"],
+        "roofline": prim["roofline"],
+        "ffn": prim["ffn"],
+        "kernels": prim["kernels"],
         "cpu_baseline": cpu,
     }
+    for k in ("down_kernel", "down_TFLOP_per_s", "layer_useful_TFLOP_per_s"):
+        if k in prim:
+            out[k] = prim[k]
     out.update(extra)
     print(json.dumps(out), flush=True)
 

@@ -283,6 +283,17 @@ moe_status moe_profile_enable(int32_t on);
 moe_status moe_profile_reset(void);
 moe_status moe_profile_read(int32_t index, const char **name, int64_t *count, double *total_ms);
 
+/* Streaming-read probe, a measurement aid (no part of the layer): one launch
+ * reads `bytes` bytes at src (device, 16-B aligned, a positive multiple of
+ * 16) with `loads_per_thread` (4, 8 or 16) 16-byte loads per thread, every
+ * load of a thread issued before any is used, and computes nothing from
+ * them.  Its kernel time (moe_profile_*, kernel "probe_read") is the time a
+ * single launch of that many bytes takes when reading is all it does, the
+ * ceiling for a bandwidth-bound kernel of the same size.  sink: device
+ * uint32 [1], written only when the loaded words happen to fold to a fixed
+ * value (it keeps the loads alive). */
+moe_status moe_probe_read(const void *src, size_t bytes, int32_t loads_per_thread, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

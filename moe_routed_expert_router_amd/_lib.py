@@ -20,7 +20,7 @@ EXPORTS = (
     "moe_workspace_bytes", "moe_residency_check", "moe_host_alloc", "moe_host_free",
     "moe_route", "moe_pick_set", "moe_gather_cold", "moe_expert_ffn", "moe_layer_forward",
     "moe_count_picks", "moe_residency_plan", "moe_residency_swap", "moe_fingerprint",
-    "moe_profile_enable", "moe_profile_reset", "moe_profile_read",
+    "moe_profile_enable", "moe_profile_reset", "moe_profile_read", "moe_probe_read",
 )
 
 MOE_OK = 0
@@ -87,6 +87,7 @@ def _load():
         "moe_profile_reset": (c_int32, []),
         "moe_profile_read": (c_int32, [c_int32, POINTER(c_char_p), POINTER(ctypes.c_int64),
                                        POINTER(ctypes.c_double)]),
+        "moe_probe_read": (c_int32, [P, c_size_t, c_int32, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -271,3 +272,7 @@ def moe_profile_read() -> dict:
             return out
         out[name.value.decode()] = (cnt.value, ms.value)
         i += 1
+
+
+def moe_probe_read(src, nbytes: int, loads_per_thread: int, sink, stream=None) -> None:
+    _check(lib.moe_probe_read(_ptr(src), nbytes, loads_per_thread, _ptr(sink), _stream(stream)))

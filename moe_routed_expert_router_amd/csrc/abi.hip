@@ -383,22 +383,15 @@ moe_status moe_expert_ffn(const moe_shape *s, int32_t T, const uint16_t *x, cons
 // gather in order with the FFN rather than beside it on a second stream.
 constexpr int kGatherOverlapMinPairs = 24;
 
-moe_status moe_layer_forward(const moe_shape *s, int32_t T, const uint16_t *x, const float *w_router,
-                             const float *bias, int32_t renormalize, const moe_residency *r, int32_t *topk_ids,
-                             float *topk_w, int32_t out_dtype, void *out, void *ws, size_t ws_bytes,
-                             void *stream) {
-    TRY(check_shape(s));
-    TRY(check_tokens(T));
-    TRY(check_residency(s, r));
-    if (T == 0) return ok();
+// The layer's launch sequence on `stream`, after the arguments were checked.
+// side_ok: the decode path with many cold picks may overlap the gather on
+// the library's side stream; otherwise everything runs in order on `stream`
+// (the same kernels and results).
+static moe_status layer_forward_enqueue(const moe_shape *s, int32_t T, const uint16_t *x, const float *w_router,
+                                        const float *bias, int32_t renormalize, const moe_residency *r,
+                                        int32_t *topk_ids, float *topk_w, int32_t out_dtype, void *out, void *ws,
+                                        void *stream, bool side_ok) {
     const int H = s->hidden, E = s->n_experts, k = s->top_k;
-    TRY(check_ptr(x, (size_t)T * H * 2, 16, "x"));
-    TRY(check_ptr(w_router, (size_t)E * H * 4, 16, "w_router"));
-    if (bias) TRY(check_ptr(bias, (size_t)E * 4, 4, "bias"));
-    TRY(check_ptr(topk_ids, (size_t)T * k * 4, 4, "topk_ids"));
-    TRY(check_ptr(topk_w, (size_t)T * k * 4, 4, "topk_w"));
-    TRY(check_out(s, T, out_dtype, out));
-    TRY(check_ws(s, T, ws, ws_bytes));
     const moe::WsLayout L = moe::WsLayout::make(H, s->inter, E, k, T);
     char *w = static_cast<char *>(ws);
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -433,7 +426,7 @@ moe_status moe_layer_forward(const moe_shape *s, int32_t T, const uint16_t *x, c
         return ok();
     }
     if (T <= moe::kSmallRouteTokens && r->n_cold > 0 && !direct && moe::ffn_block_path(T, H, s->inter) &&
-        T * k <= kGatherOverlapMinPairs) {
+        (T * k <= kGatherOverlapMinPairs || !side_ok)) {
         // a few tokens with cold experts, in order on the caller's stream:
         // select and group, the hot experts' FFN, the gather of the published
         // cold list, the cold experts' FFN and the combine.  Measured per
@@ -488,6 +481,35 @@ moe_status moe_layer_forward(const moe_shape *s, int32_t T, const uint16_t *x, c
         TRY(hip_status(moe::launch_gather(r->host_cold, r->scratch, g.blob_bytes, r->slot, w, L, st),
                        "gather launch"));
     TRY(enqueue_ffn(s, T, x, topk_ids, topk_w, out_dtype, out, w, L, st));
+    return ok();
+}
+
+static moe_status check_layer_args(const moe_shape *s, int32_t T, const uint16_t *x, const float *w_router,
+                                   const float *bias, const moe_residency *r, int32_t *topk_ids, float *topk_w,
+                                   int32_t out_dtype, void *out) {
+    TRY(check_shape(s));
+    TRY(check_tokens(T));
+    TRY(check_residency(s, r));
+    if (T == 0) return MOE_OK;
+    const int H = s->hidden, E = s->n_experts, k = s->top_k;
+    TRY(check_ptr(x, (size_t)T * H * 2, 16, "x"));
+    TRY(check_ptr(w_router, (size_t)E * H * 4, 16, "w_router"));
+    if (bias) TRY(check_ptr(bias, (size_t)E * 4, 4, "bias"));
+    TRY(check_ptr(topk_ids, (size_t)T * k * 4, 4, "topk_ids"));
+    TRY(check_ptr(topk_w, (size_t)T * k * 4, 4, "topk_w"));
+    TRY(check_out(s, T, out_dtype, out));
+    return MOE_OK;
+}
+
+moe_status moe_layer_forward(const moe_shape *s, int32_t T, const uint16_t *x, const float *w_router,
+                             const float *bias, int32_t renormalize, const moe_residency *r, int32_t *topk_ids,
+                             float *topk_w, int32_t out_dtype, void *out, void *ws, size_t ws_bytes,
+                             void *stream) {
+    TRY(check_layer_args(s, T, x, w_router, bias, r, topk_ids, topk_w, out_dtype, out));
+    if (T == 0) return ok();
+    TRY(check_ws(s, T, ws, ws_bytes));
+    TRY(layer_forward_enqueue(s, T, x, w_router, bias, renormalize, r, topk_ids, topk_w, out_dtype, out, ws, stream,
+                              true));
     return ok();
 }
 
@@ -575,6 +597,18 @@ moe_status moe_fingerprint(const moe_shape *s, const moe_residency *r, const int
     TRY(hip_status(moe::launch_fingerprint(experts, n, r->slot, r->hot_base, r->host_cold, B, s->n_experts, r->n_hot,
                                            r->n_cold, out, static_cast<hipStream_t>(stream)),
                    "fingerprint launch"));
+    return ok();
+}
+
+moe_status moe_probe_read(const void *src, size_t bytes, int32_t loads_per_thread, uint32_t *sink, void *stream) {
+    if (bytes == 0 || bytes % 16 || bytes > ((size_t)1 << 40))
+        return fail(MOE_ERR_INVALID_ARG, "bytes %zu must be a positive multiple of 16", bytes);
+    if (loads_per_thread != 4 && loads_per_thread != 8 && loads_per_thread != 16)
+        return fail(MOE_ERR_INVALID_ARG, "loads_per_thread %d must be 4, 8 or 16", loads_per_thread);
+    TRY(check_ptr(src, bytes, 16, "src"));
+    TRY(check_ptr(sink, 4, 4, "sink"));
+    TRY(hip_status(moe::launch_probe_read(src, bytes, loads_per_thread, sink, static_cast<hipStream_t>(stream)),
+                   "probe launch"));
     return ok();
 }
 

@@ -147,6 +147,11 @@ hipError_t launch_fingerprint(const int32_t *experts, int n, const int32_t *slot
                               const uint8_t *host_cold, size_t blob_bytes, int E, int n_hot, int n_cold,
                               uint64_t *out, hipStream_t st);
 
+// Streaming read of `bytes` (a multiple of 16) from src by one launch with
+// `loads_per_thread` (4, 8 or 16) 16-byte loads per thread; writes nothing.
+hipError_t launch_probe_read(const void *src, size_t bytes, int loads_per_thread, uint32_t *sink,
+                             hipStream_t st);
+
 // Host side of the manager: decayed scores and the swap rule; returns the
 // number of pairs written to pairs[2*i], pairs[2*i+1] and updates slot and score.
 int plan_swaps(int E, int32_t *slot, double *score, const int32_t *counts, double decay, double threshold,
