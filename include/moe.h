@@ -204,6 +204,25 @@ moe_status moe_layer_forward(const moe_shape *s, int32_t n_tokens, const uint16_
                              int32_t out_dtype, void *out,
                              void *ws, size_t ws_bytes, void *stream);
 
+/* moe_layer_forward for callers that cannot allocate (code under graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * layer with the same results, but no caller workspace and no allocation
+ * of any kind.  Its workspace is a static device array of
+ * MOE_NOALLOC_WS_BYTES bytes inside the library, one per GPU it runs on,
+ * held until the process ends; T tokens need moe_workspace_bytes(s, T)
+ * bytes of it (16 MiB covers up to ~110 decode tokens at H=4096, I=2048,
+ * E=384, k=6), and larger calls return MOE_ERR_WORKSPACE_TOO_SMALL with
+ * nothing enqueued.  Everything runs on `stream` (no side stream), in the
+ * in-order launch sequence.  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (two streams, two threads) race and must be
+ * ordered by the caller.  With moe_profile_enable on, the timing events are
+ * still created as for every entry point. */
+#define MOE_NOALLOC_WS_BYTES (16u << 20)
+moe_status moe_layer_forward_noalloc(const moe_shape *s, int32_t n_tokens, const uint16_t *x,
+                                     const float *w_router, const float *bias, int32_t renormalize,
+                                     const moe_residency *r, int32_t *topk_ids, float *topk_w,
+                                     int32_t out_dtype, void *out, void *stream);
+
 /* ---------------------------------------------------------------------------
  * Adaptive residency and the byte audit.  The gracetier write-up: between
  * decode steps a manager swaps experts that are being picked often into the

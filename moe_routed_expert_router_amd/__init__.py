@@ -14,4 +14,5 @@ from ._lib import (  # noqa: F401
     moe_gather_cold, moe_expert_ffn, moe_layer_forward,
     MOE_MAX_SWAPS, moe_count_picks, moe_residency_plan, moe_residency_swap, moe_fingerprint,
     moe_profile_enable, moe_profile_reset, moe_profile_read, moe_probe_read,
+    MOE_NOALLOC_WS_BYTES, moe_layer_forward_noalloc,
 )

@@ -21,6 +21,7 @@ EXPORTS = (
     "moe_route", "moe_pick_set", "moe_gather_cold", "moe_expert_ffn", "moe_layer_forward",
     "moe_count_picks", "moe_residency_plan", "moe_residency_swap", "moe_fingerprint",
     "moe_profile_enable", "moe_profile_reset", "moe_profile_read", "moe_probe_read",
+    "moe_layer_forward_noalloc",
 )
 
 MOE_OK = 0
@@ -88,6 +89,8 @@ def _load():
         "moe_profile_read": (c_int32, [c_int32, POINTER(c_char_p), POINTER(ctypes.c_int64),
                                        POINTER(ctypes.c_double)]),
         "moe_probe_read": (c_int32, [P, c_size_t, c_int32, P, P]),
+        "moe_layer_forward_noalloc": (c_int32, [POINTER(MoeShape), c_int32, P, P, P, c_int32,
+                                                POINTER(MoeResidency), P, P, c_int32, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -213,6 +216,16 @@ def moe_layer_forward(s: MoeShape, x, w_router, bias, renormalize: bool, r: MoeR
     _check(lib.moe_layer_forward(ctypes.byref(s), T, _ptr(x), _ptr(w_router), _ptr(bias), int(bool(renormalize)),
                                  ctypes.byref(r), _ptr(topk_ids), _ptr(topk_w), _out_dtype(out), _ptr(out),
                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+MOE_NOALLOC_WS_BYTES = 16 << 20
+
+
+def moe_layer_forward_noalloc(s: MoeShape, x, w_router, bias, renormalize: bool, r: MoeResidency, topk_ids,
+                              topk_w, out, stream=None) -> None:
+    _check(lib.moe_layer_forward_noalloc(ctypes.byref(s), x.shape[0], _ptr(x), _ptr(w_router), _ptr(bias),
+                                         1 if renormalize else 0, ctypes.byref(r), _ptr(topk_ids), _ptr(topk_w),
+                                         _out_dtype(out), _ptr(out), _stream(stream)))
 
 
 MOE_MAX_SWAPS = 64

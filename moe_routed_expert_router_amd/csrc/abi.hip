@@ -200,6 +200,39 @@ moe_status side_stream(std::unique_lock<std::mutex> &lock, SideStream **out) {
     return MOE_OK;
 }
 
+// Workspace of moe_layer_forward_noalloc: a file-scope device array, one
+// copy per GPU the library runs on, held until the process ends.  Its host-
+// side name is not a device address: the kernels get the address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device on that entry point's first call there.
+static __device__ __align__(256) uint8_t noalloc_scratch[MOE_NOALLOC_WS_BYTES];
+
+struct NoallocWs {
+    std::once_flag once;
+    hipError_t err = hipSuccess;
+    void *ptr = nullptr;
+};
+NoallocWs g_noalloc[kMaxDevices];
+
+moe_status noalloc_ws(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return fail(MOE_ERR_HIP, "no usable current device for the static workspace");
+    }
+    NoallocWs &w = g_noalloc[dev];
+    std::call_once(w.once, [&w] {
+        void *p = nullptr;
+        w.err = hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc_scratch));
+        w.ptr = w.err == hipSuccess ? p : nullptr;
+        if (w.err != hipSuccess) (void)hipGetLastError();
+    });
+    if (w.err != hipSuccess || w.ptr == nullptr)
+        return fail(MOE_ERR_HIP, "static workspace address on device %d: %s", dev, hipGetErrorString(w.err));
+    *out = w.ptr;
+    return MOE_OK;
+}
+
 moe_status check_out(const moe_shape *s, int32_t T, int32_t out_dtype, void *out) {
     if (out_dtype != MOE_OUT_F32 && out_dtype != MOE_OUT_BF16)
         return fail(MOE_ERR_INVALID_ARG, "out_dtype %d unknown", out_dtype);
@@ -510,6 +543,23 @@ moe_status moe_layer_forward(const moe_shape *s, int32_t T, const uint16_t *x, c
     TRY(check_ws(s, T, ws, ws_bytes));
     TRY(layer_forward_enqueue(s, T, x, w_router, bias, renormalize, r, topk_ids, topk_w, out_dtype, out, ws, stream,
                               true));
+    return ok();
+}
+
+moe_status moe_layer_forward_noalloc(const moe_shape *s, int32_t T, const uint16_t *x, const float *w_router,
+                                     const float *bias, int32_t renormalize, const moe_residency *r,
+                                     int32_t *topk_ids, float *topk_w, int32_t out_dtype, void *out, void *stream) {
+    TRY(check_layer_args(s, T, x, w_router, bias, r, topk_ids, topk_w, out_dtype, out));
+    if (T == 0) return ok();
+    const size_t need = moe::WsLayout::make(s->hidden, s->inter, s->n_experts, s->top_k, T).total;
+    if (need > (size_t)MOE_NOALLOC_WS_BYTES)
+        return fail(MOE_ERR_WORKSPACE_TOO_SMALL,
+                    "%d tokens need a %zu-byte workspace; the static one holds %zu (use moe_layer_forward)", T,
+                    need, (size_t)MOE_NOALLOC_WS_BYTES);
+    void *ws = nullptr;
+    TRY(noalloc_ws(&ws));
+    TRY(layer_forward_enqueue(s, T, x, w_router, bias, renormalize, r, topk_ids, topk_w, out_dtype, out, ws, stream,
+                              false));
     return ok();
 }
 
