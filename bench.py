@@ -1141,12 +1141,24 @@ def main():
     ap.add_argument("--no-ffn-batches", action="store_true",
                     help="skip the standalone grouped-FFN figures at batch 1/8/32")
     ap.add_argument("--no-step40", action="store_true", help="skip the 40-layer batch-32 secondary figures")
+    ap.add_argument("--only", default=None,
+                    help="run only this secondary figure (read_ceiling, prefill8k, batch8_hotcold, direct_read, "
+                         "adaptive_residency, verify, gather_sweep, layer_copy, ffn_by_batch, step40_batch32)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-layer secondary figures")
     ap.add_argument("--no-read-ceiling", action="store_true", help="skip the streaming-read ceiling probe")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="first run one plain float64 copy of this many MiB (a known-size kernel for "
                          "scaling hardware byte counters)")
     a = ap.parse_args()
+    keys = {"read_ceiling": "no_read_ceiling", "prefill8k": "no_prefill", "batch8_hotcold": "no_batch8",
+            "direct_read": "no_direct_read", "adaptive_residency": "no_adaptive", "verify": "no_verify",
+            "gather_sweep": "no_gather_sweep", "layer_copy": "no_layer_copy", "ffn_by_batch": "no_ffn_batches",
+            "step40_batch32": "no_step40"}
+    if a.only is not None:
+        if a.only not in keys:
+            ap.error(f"--only: unknown secondary {a.only}")
+        for k, flag in keys.items():
+            setattr(a, flag, k != a.only)
     if a.primary_only:
         for k in ("no_batch8", "no_adaptive", "no_verify", "no_layer_copy", "no_direct_read", "no_ffn_batches",
                   "no_step40", "no_gather_sweep", "no_prefill", "no_read_ceiling"):
@@ -1222,7 +1234,7 @@ def main():
                       measure_read_ceiling)
         if not a.no_prefill:
             secondary("prefill8k", "prefill layer (8192 tokens, all resident, grouped GEMM)", prefill)
-        if not a.primary_only:
+        if not a.primary_only and a.only is None:
             secondary("host_call", "host time of one eager moe_layer_forward (decode1)", measure_host_call)
         if not a.no_batch8:
             secondary("batch8_hotcold", "hotcold8 (batch 8, 255 hot / 129 cold)", batch8)

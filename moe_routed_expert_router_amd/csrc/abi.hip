@@ -2,9 +2,9 @@
 // kernel launches on the caller's stream.  Nothing is enqueued after a failed
 // check (the 96 GB RTX PRO 6000 write-up, "Five layers made the difference",
 // audits its host pages and pointers and fails startup when the geometry is
-// wrong; the GB300 write-up's flag table records a parameter pattern that
-// "silently matches nothing" — every malformed input here is an explicit
-// status instead).
+// wrong; the inference-engineering write-up's flag table records a setting
+// whose pattern matched no parameter at all without any error — every
+// malformed input here is an explicit status instead).
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>

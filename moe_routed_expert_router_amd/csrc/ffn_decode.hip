@@ -1,7 +1,7 @@
 // Grouped SwiGLU expert FFN and weighted combine.
 //
-// The gracetier write-up (section 1) runs every picked expert "in a single
-// call, as if they had been in HBM all along": a blob-address table from the
+// The gracetier write-up (section 1) runs every picked expert in one call,
+// as though all of them were resident in HBM: a blob-address table from the
 // grouping points each distinct expert at its HBM home or its scratch slot,
 // and the kernels never look at residency again, so an all-hot run and a
 // mixed hot/cold run execute identical instructions on identical bytes.

@@ -1,8 +1,8 @@
 // Router: logits and top-k softmax selection, plus the fused select-and-group
 // kernel of the decode path.
 //
-// The pages: a tiny router picks the 6 most relevant of 384 experts per token
-// (GB300 inference write-up, mixture-of-experts paragraph).  Scores are a
+// The pages: per token a small router chooses 6 of the 384 experts (the
+// inference-engineering write-up, mixture-of-experts paragraph).  Scores are a
 // softmax over z[t,e] = x_t . Wr_e + b_e; the k largest logits are kept, equal
 // logits going to the lower expert index, and the kept weights renormalised.
 #include "kernels.hpp"

@@ -1,8 +1,8 @@
 """Router: logits, top-k selection and routing weights.
 
-The pages: "for each token a tiny router picks the 6 most relevant" of 384
-experts (GB300 inference-engineering write-up, first paragraph on the
-mixture-of-experts design).  They give no score function; the readings taken:
+The pages: per token a small router chooses 6 of the 384 experts (the
+inference-engineering write-up, "Milo and James try inference engineering",
+first paragraph on the mixture-of-experts design).  They give no score function; the readings taken:
 
   * scores are a softmax over the E logits z[t,e] = sum_h x[t,h] Wr[e,h] + b[e],
     b an optional logit prior (the synthetic Zipf bias), added before softmax;
