@@ -397,12 +397,15 @@ def layer_figures(name: str, steps: int, warmup: int, reps: int, use_graph: bool
         torch.cuda.empty_cache()
 
 
-def measure_read_ceiling(sizes=(26886144, 53534720, 80420864), launches: int = 24) -> dict:
+def measure_read_ceiling(sizes=(6291456, 26886144, 53534720, 80420864), launches: int = 24,
+                         repeated=(6291456,)) -> dict:
     """The single-launch streaming-read ceiling: moe_probe_read over fresh
-    bytes at each size (the decode1 down, gate/up and whole-FFN volumes),
-    launches rotating over a pool larger than the Infinity Cache, kernel time
-    from the library's launch events; the best of 4, 8 and 16 loads per
-    thread, with the median of the launches."""
+    bytes at each size (the decode1 router, down, gate/up and whole-FFN
+    volumes), launches rotating over a pool larger than the Infinity Cache,
+    kernel time from the library's launch events; the best of 1, 2, 4, 8 and
+    16 loads per thread, with the median of the launches.  Sizes in
+    `repeated` are measured again reading the same bytes every launch (as the
+    router reads its weights every step), which the Infinity Cache can hold."""
     import torch
     import moe_routed_expert_router_amd as moe
     pool_bytes = max(1 << 30, 12 * max(sizes))
@@ -410,34 +413,39 @@ def measure_read_ceiling(sizes=(26886144, 53534720, 80420864), launches: int = 2
     pool.fill_(0x5A)
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     out = {}
-    try:
-        for n in sizes:
-            n16 = n // 16 * 16
-            slots = pool_bytes // n16
-            best = None
-            for lpt in (4, 8, 16):
-                for i in range(4):   # untimed
-                    moe.moe_probe_read(pool[(i % slots) * n16:], n16, lpt, sink)
+
+    def one(n16, rotate):
+        slots = pool_bytes // n16 if rotate else 1
+        best = None
+        for lpt in (1, 2, 4, 8, 16):
+            for i in range(4):   # untimed
+                moe.moe_probe_read(pool[(i % slots) * n16:], n16, lpt, sink)
+            torch.cuda.synchronize()
+            us = []
+            for i in range(launches):
+                moe.moe_profile_reset()
+                moe.moe_profile_enable(True)
+                moe.moe_probe_read(pool[(i % slots) * n16:], n16, lpt, sink)
                 torch.cuda.synchronize()
-                us = []
-                for i in range(launches):
-                    moe.moe_profile_reset()
-                    moe.moe_profile_enable(True)
-                    moe.moe_probe_read(pool[(i % slots) * n16:], n16, lpt, sink)
-                    torch.cuda.synchronize()
-                    moe.moe_profile_enable(False)
-                    cnt, ms = moe.moe_profile_read()["probe_read"]
-                    us.append(1e3 * ms / cnt)
-                med = float(np.median(us))
-                if best is None or med < best[1]:
-                    best = (lpt, med, spread(us))
-            lpt, med, sp = best
+                moe.moe_profile_enable(False)
+                cnt, ms = moe.moe_profile_read()["probe_read"]
+                us.append(1e3 * ms / cnt)
+            med = float(np.median(us))
+            if best is None or med < best[1]:
+                best = (lpt, med, spread(us))
+        return best
+
+    try:
+        for n, rotate in [(n, True) for n in sizes] + [(n, False) for n in repeated]:
+            n16 = n // 16 * 16
+            lpt, med, sp = one(n16, rotate)
             gbs = n16 / (med * 1e-6) / 1e9
-            out[f"{n16 / 1e6:.1f}MB"] = {"bytes": n16, "loads_per_thread": lpt, "kernel_us": round(med, 3),
-                                         "GB_per_s": round(gbs, 1), "frac_of_hbm": round(gbs / HBM_PEAK_GBS, 4),
-                                         "spread": round(sp, 4)}
-            log(f"[bench] read ceiling {n16 / 1e6:6.1f} MB: {med:7.2f} us = {gbs:7.1f} GB/s "
-                f"({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s), {lpt} loads/thread")
+            key = f"{n16 / 1e6:.1f}MB" + ("" if rotate else "_repeated")
+            out[key] = {"bytes": n16, "loads_per_thread": lpt, "kernel_us": round(med, 3),
+                        "GB_per_s": round(gbs, 1), "frac_of_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                        "spread": round(sp, 4)}
+            log(f"[bench] read ceiling {n16 / 1e6:6.1f} MB{'' if rotate else ' (same bytes each launch)'}: "
+                f"{med:7.2f} us = {gbs:7.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s), {lpt} loads/thread")
         return out
     finally:
         moe.moe_profile_reset()
@@ -1230,7 +1238,7 @@ def main():
 
     if a.workload == "decode1":
         if not a.no_read_ceiling:
-            secondary("read_ceiling", "single-launch streaming-read ceiling (26.9 / 53.5 / 80.4 MB)",
+            secondary("read_ceiling", "single-launch streaming-read ceiling (6.3 / 26.9 / 53.5 / 80.4 MB)",
                       measure_read_ceiling)
         if not a.no_prefill:
             secondary("prefill8k", "prefill layer (8192 tokens, all resident, grouped GEMM)", prefill)

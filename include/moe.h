@@ -324,7 +324,7 @@ moe_status moe_profile_read(int32_t index, const char **name, int64_t *count, do
 
 /* Streaming-read probe, a measurement aid (no part of the layer): one launch
  * reads `bytes` bytes at src (device, 16-B aligned, a positive multiple of
- * 16) with `loads_per_thread` (4, 8 or 16) 16-byte loads per thread, every
+ * 16) with `loads_per_thread` (1, 2, 4, 8 or 16) 16-byte loads per thread, every
  * load of a thread issued before any is used, and computes nothing from
  * them.  Its kernel time (moe_profile_*, kernel "probe_read") is the time a
  * single launch of that many bytes takes when reading is all it does, the

@@ -653,8 +653,9 @@ moe_status moe_fingerprint(const moe_shape *s, const moe_residency *r, const int
 moe_status moe_probe_read(const void *src, size_t bytes, int32_t loads_per_thread, uint32_t *sink, void *stream) {
     if (bytes == 0 || bytes % 16 || bytes > ((size_t)1 << 40))
         return fail(MOE_ERR_INVALID_ARG, "bytes %zu must be a positive multiple of 16", bytes);
-    if (loads_per_thread != 4 && loads_per_thread != 8 && loads_per_thread != 16)
-        return fail(MOE_ERR_INVALID_ARG, "loads_per_thread %d must be 4, 8 or 16", loads_per_thread);
+    if (loads_per_thread != 1 && loads_per_thread != 2 && loads_per_thread != 4 && loads_per_thread != 8 &&
+        loads_per_thread != 16)
+        return fail(MOE_ERR_INVALID_ARG, "loads_per_thread %d must be 1, 2, 4, 8 or 16", loads_per_thread);
     TRY(check_ptr(src, bytes, 16, "src"));
     TRY(check_ptr(sink, 4, 4, "sink"));
     TRY(hip_status(moe::launch_probe_read(src, bytes, loads_per_thread, sink, static_cast<hipStream_t>(stream)),

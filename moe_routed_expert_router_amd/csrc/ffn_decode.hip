@@ -21,8 +21,9 @@
 //   gate/up: 8 waves = {gate, up} x RT row tiles x K slices (RT = 1 below 8
 //            tokens, 2 from 8 tokens on, so that one staging of the token
 //            rows serves twice the weight rows); each wave issues all of its
-//            slice's weight loads at once (memory-level parallelism comes
-//            from many small independent waves, not deep per-wave pipelines);
+//            slice's weight loads at once, before the token rows (memory-
+//            level parallelism comes from many small independent waves, not
+//            deep per-wave pipelines);
 //            tokens are staged once per block in LDS; the slice partials are
 //            added in a fixed order in LDS; h = silu(g) * u is stored as bf16
 //            hi + lo parts (h - hi rounded again), ~16 significant bits.
@@ -129,17 +130,29 @@ __device__ __forceinline__ void gate_up_tile_blk(const uint16_t *__restrict__ x,
     uint4 *xs = reinterpret_cast<uint4 *>(smem);
     f32x4 *red = reinterpret_cast<f32x4 *>(smem + (size_t)NT * stride * 16);
 
-    // The first pass's token rows go to LDS by DMA ahead of the weight loads
-    // (one 1 KB fill per wave and row, no registers held).  The vector memory
-    // counter retires in issue order, so waiting for the fills leaves the
-    // weights in flight, and the MFMAs then wait for the codes step by step.
+    // Weights first: every weight load of this wave's slice goes out as soon
+    // as the expert is known, preceded only by the read of the first pass's
+    // pair ids (the oldest load, so using them waits for no weight).  The
+    // token rows then go to LDS by DMA (one 1 KB fill per wave and row, no
+    // registers held); the vector memory counter retires in issue order, so
+    // the MFMAs start once the fills, and with them every weight, are in.
+    // Against fills first and weights after, this sends the weights one
+    // round trip (the pair ids) earlier.
     const bool dma = nch % 64 == 0 && nch / 64 <= nw;
     const int ndma = (n < NT ? n : NT) < kDmaRows ? (n < NT ? n : NT) : kDmaRows;
+    uint4 q[SPW];
+    uint32_t sc[SPW];
+    int my_tok = 0;   // lane c < ndma: pair id of token row c
+    if (dma && wave < nch / 64) my_tok = pair_of(lane < ndma ? lane : ndma - 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) q[i] = gload16(qp + (size_t)i * 64);
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) sc[i] = gload<uint32_t>(sp + 4 * i);
+    __builtin_amdgcn_sched_barrier(0);
     if (dma && wave < nch / 64) {
         const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(x, 0xFFFFFFF0u);
-        // the rows' pair ids in one round: lane c reads row c's, then each
-        // row's token is broadcast from its lane
-        const int my_tok = pair_of(lane < ndma ? lane : ndma - 1) / k;
+        my_tok /= k;
 #pragma unroll
         for (int c = 0; c < kDmaRows; ++c)
             if (c < ndma) {
@@ -149,15 +162,6 @@ __device__ __forceinline__ void gate_up_tile_blk(const uint16_t *__restrict__ x,
             }
     }
     __builtin_amdgcn_sched_barrier(0);
-    // every weight load of this wave's slice, in flight together: codes,
-    // then scales (the fills' wait counts both as still outstanding)
-    uint4 q[SPW];
-    uint32_t sc[SPW];
-#pragma unroll
-    for (int i = 0; i < SPW; ++i) q[i] = gload16(qp + (size_t)i * 64);
-#pragma unroll
-    for (int i = 0; i < SPW; ++i) sc[i] = gload<uint32_t>(sp + 4 * i);
-    __builtin_amdgcn_sched_barrier(0);
 
     for (int tb = 0; tb < n; tb += NT) {
         const int nt = (n - tb) < NT ? (n - tb) : NT;
@@ -166,9 +170,7 @@ __device__ __forceinline__ void gate_up_tile_blk(const uint16_t *__restrict__ x,
                 const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)(pair_of(c) / k) * H);
                 for (int j = tid; j < nch; j += blockDim.x) xs[c * stride + j] = src[j];
             }
-            // the weight loads retire after the fills; the scales may have
-            // been merged into as few as SPW/4 loads
-            fill_barrier<SPW + (SPW + 3) / 4>();
+            fill_barrier<0>();   // fills and weights
         } else {
             __syncthreads();
             for (int c = 0; c < nt; ++c) {

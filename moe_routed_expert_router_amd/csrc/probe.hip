@@ -37,6 +37,8 @@ hipError_t launch_probe_read(const void *src, size_t bytes, int loads_per_thread
     const dim3 g((unsigned)((units + per_block - 1) / per_block)), b(kProbeThreads);
     const u32x4 *s = static_cast<const u32x4 *>(src);
     switch (loads_per_thread) {
+        case 1: MOE_LAUNCH("probe_read", probe_read<1>, g, b, 0, st, s, units, 0x5EEDF00Du, sink); break;
+        case 2: MOE_LAUNCH("probe_read", probe_read<2>, g, b, 0, st, s, units, 0x5EEDF00Du, sink); break;
         case 4: MOE_LAUNCH("probe_read", probe_read<4>, g, b, 0, st, s, units, 0x5EEDF00Du, sink); break;
         case 8: MOE_LAUNCH("probe_read", probe_read<8>, g, b, 0, st, s, units, 0x5EEDF00Du, sink); break;
         default: MOE_LAUNCH("probe_read", probe_read<16>, g, b, 0, st, s, units, 0x5EEDF00Du, sink); break;
