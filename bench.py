@@ -453,6 +453,55 @@ def measure_read_ceiling(sizes=(6291456, 26886144, 53534720, 80420864), launches
         torch.cuda.empty_cache()
 
 
+MFMA_KINDS = (   # (name, flops per instruction, published dense peak TFLOP/s or None)
+    ("bf16 32x32x16", 32768, 2500.0),
+    ("f8f6f4 32x32x64 fp8 x fp4", 131072, None),
+    ("f8f6f4 32x32x64 fp8 x fp8", 131072, 5000.0),
+    ("f8f6f4 32x32x64 fp6 x fp4", 131072, None),
+    ("f8f6f4 32x32x64 fp4 x fp4", 131072, 10100.0),
+)
+
+
+def measure_mfma_rates(iters: int = 4096, launches: int = 5) -> dict:
+    """Matrix-core rate of bf16 and of the scaled f8f6f4 forms with the GPU
+    full (moe_probe_mfma: two 4-wave blocks per CU, four independent MFMAs
+    per round), kernel time from the library's launch events, median of the
+    launches.  The prefill gate/up would take x as a two-term fp8 split
+    against fp4 weights: two fp8 x fp4 instructions per 32x32x64 step."""
+    import torch
+    import moe_routed_expert_router_amd as moe
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    waves = 2 * cus * 4
+    out = {}
+    try:
+        base = None
+        for kind, (name, fpi, peak) in enumerate(MFMA_KINDS):
+            for _ in range(2):   # untimed
+                moe.moe_probe_mfma(kind, iters, sink)
+            torch.cuda.synchronize()
+            us = []
+            for _ in range(launches):
+                moe.moe_profile_reset()
+                moe.moe_profile_enable(True)
+                moe.moe_probe_mfma(kind, iters, sink)
+                torch.cuda.synchronize()
+                moe.moe_profile_enable(False)
+                cnt, ms = moe.moe_profile_read()["probe_mfma"]
+                us.append(1e3 * ms / cnt)
+            med = float(np.median(us))
+            tfs = waves * iters * 4 * fpi / (med * 1e-6) / 1e12
+            base = base or tfs
+            out[name] = {"kernel_us": round(med, 2), "TFLOP_per_s": round(tfs, 1), "vs_bf16": round(tfs / base, 3),
+                         "frac_of_published_peak": round(tfs / peak, 3) if peak else None,
+                         "spread": round(spread(us), 4)}
+            log(f"[bench] mfma {name:28s}: {tfs:8.1f} TFLOP/s ({tfs / base:.2f}x bf16"
+                + (f", {100 * tfs / peak:.0f}% of {peak / 1000:.1f} PFLOP/s" if peak else "") + ")")
+        return out
+    finally:
+        moe.moe_profile_reset()
+
+
 def measure_host_call(name: str = "decode1", calls: int = 200) -> dict:
     """Host time of one eager moe_layer_forward call (argument checks,
     pointer lookups and launches; the call does not wait for the GPU)."""
@@ -1150,15 +1199,16 @@ def main():
                     help="skip the standalone grouped-FFN figures at batch 1/8/32")
     ap.add_argument("--no-step40", action="store_true", help="skip the 40-layer batch-32 secondary figures")
     ap.add_argument("--only", default=None,
-                    help="run only this secondary figure (read_ceiling, prefill8k, batch8_hotcold, direct_read, "
+                    help="run only this secondary figure (read_ceiling, mfma_rates, prefill8k, batch8_hotcold, direct_read, "
                          "adaptive_residency, verify, gather_sweep, layer_copy, ffn_by_batch, step40_batch32)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-layer secondary figures")
     ap.add_argument("--no-read-ceiling", action="store_true", help="skip the streaming-read ceiling probe")
+    ap.add_argument("--no-mfma-rates", action="store_true", help="skip the matrix-core rate probe")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="first run one plain float64 copy of this many MiB (a known-size kernel for "
                          "scaling hardware byte counters)")
     a = ap.parse_args()
-    keys = {"read_ceiling": "no_read_ceiling", "prefill8k": "no_prefill", "batch8_hotcold": "no_batch8",
+    keys = {"read_ceiling": "no_read_ceiling", "mfma_rates": "no_mfma_rates", "prefill8k": "no_prefill", "batch8_hotcold": "no_batch8",
             "direct_read": "no_direct_read", "adaptive_residency": "no_adaptive", "verify": "no_verify",
             "gather_sweep": "no_gather_sweep", "layer_copy": "no_layer_copy", "ffn_by_batch": "no_ffn_batches",
             "step40_batch32": "no_step40"}
@@ -1169,7 +1219,7 @@ def main():
             setattr(a, flag, k != a.only)
     if a.primary_only:
         for k in ("no_batch8", "no_adaptive", "no_verify", "no_layer_copy", "no_direct_read", "no_ffn_batches",
-                  "no_step40", "no_gather_sweep", "no_prefill", "no_read_ceiling"):
+                  "no_step40", "no_gather_sweep", "no_prefill", "no_read_ceiling", "no_mfma_rates"):
             setattr(a, k, True)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -1240,6 +1290,8 @@ def main():
         if not a.no_read_ceiling:
             secondary("read_ceiling", "single-launch streaming-read ceiling (6.3 / 26.9 / 53.5 / 80.4 MB)",
                       measure_read_ceiling)
+        if not a.no_mfma_rates:
+            secondary("mfma_rates", "matrix-core rates: bf16 and scaled f8f6f4 forms, GPU full", measure_mfma_rates)
         if not a.no_prefill:
             secondary("prefill8k", "prefill layer (8192 tokens, all resident, grouped GEMM)", prefill)
         if not a.primary_only and a.only is None:

@@ -333,6 +333,18 @@ moe_status moe_profile_read(int32_t index, const char **name, int64_t *count, do
  * value (it keeps the loads alive). */
 moe_status moe_probe_read(const void *src, size_t bytes, int32_t loads_per_thread, uint32_t *sink, void *stream);
 
+/* Matrix-core rate probe, a measurement aid (no part of the layer): one
+ * launch of two 256-thread blocks per compute unit in which every wave
+ * issues `iters` (1..2^20) rounds of four independent MFMAs of one kind on
+ * register operands.  kind: 0 bf16 32x32x16 (32768 flops per instruction);
+ * the gfx950 scaled 32x32x64 f8f6f4 form (131072 flops) with operands 1 fp8
+ * x fp4, 2 fp8 x fp8, 3 fp6 (e2m3) x fp4, 4 fp4 x fp4.  The kernel time
+ * (moe_profile_*, kernel "probe_mfma") gives the rate each kind sustains
+ * with the GPU full.  sink: device uint32 [1], written only when the
+ * accumulators fold to a fixed value.  MOE_ERR_INVALID_ARG for a kind or
+ * iters out of range. */
+moe_status moe_probe_mfma(int32_t kind, int32_t iters, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -13,6 +13,6 @@ from ._lib import (  # noqa: F401
     moe_residency_check, moe_host_alloc, moe_host_free, moe_route, moe_pick_set,
     moe_gather_cold, moe_expert_ffn, moe_layer_forward,
     MOE_MAX_SWAPS, moe_count_picks, moe_residency_plan, moe_residency_swap, moe_fingerprint,
-    moe_profile_enable, moe_profile_reset, moe_profile_read, moe_probe_read,
+    moe_profile_enable, moe_profile_reset, moe_profile_read, moe_probe_read, moe_probe_mfma,
     MOE_NOALLOC_WS_BYTES, moe_layer_forward_noalloc,
 )

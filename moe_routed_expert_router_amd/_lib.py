@@ -20,7 +20,7 @@ EXPORTS = (
     "moe_workspace_bytes", "moe_residency_check", "moe_host_alloc", "moe_host_free",
     "moe_route", "moe_pick_set", "moe_gather_cold", "moe_expert_ffn", "moe_layer_forward",
     "moe_count_picks", "moe_residency_plan", "moe_residency_swap", "moe_fingerprint",
-    "moe_profile_enable", "moe_profile_reset", "moe_profile_read", "moe_probe_read",
+    "moe_profile_enable", "moe_profile_reset", "moe_profile_read", "moe_probe_read", "moe_probe_mfma",
     "moe_layer_forward_noalloc",
 )
 
@@ -89,6 +89,7 @@ def _load():
         "moe_profile_read": (c_int32, [c_int32, POINTER(c_char_p), POINTER(ctypes.c_int64),
                                        POINTER(ctypes.c_double)]),
         "moe_probe_read": (c_int32, [P, c_size_t, c_int32, P, P]),
+        "moe_probe_mfma": (c_int32, [c_int32, c_int32, P, P]),
         "moe_layer_forward_noalloc": (c_int32, [POINTER(MoeShape), c_int32, P, P, P, c_int32,
                                                 POINTER(MoeResidency), P, P, c_int32, P, P]),
     }
@@ -289,3 +290,7 @@ def moe_profile_read() -> dict:
 
 def moe_probe_read(src, nbytes: int, loads_per_thread: int, sink, stream=None) -> None:
     _check(lib.moe_probe_read(_ptr(src), nbytes, loads_per_thread, _ptr(sink), _stream(stream)))
+
+
+def moe_probe_mfma(kind: int, iters: int, sink, stream=None) -> None:
+    _check(lib.moe_probe_mfma(kind, iters, _ptr(sink), _stream(stream)))

@@ -663,4 +663,15 @@ moe_status moe_probe_read(const void *src, size_t bytes, int32_t loads_per_threa
     return ok();
 }
 
+moe_status moe_probe_mfma(int32_t kind, int32_t iters, uint32_t *sink, void *stream) {
+    if (kind < 0 || kind > 4) return fail(MOE_ERR_INVALID_ARG, "kind %d must be 0..4", kind);
+    if (iters < 1 || iters > (1 << 20)) return fail(MOE_ERR_INVALID_ARG, "iters %d must be 1..2^20", iters);
+    TRY(check_ptr(sink, 4, 4, "sink"));
+    int dev = 0, cus = 0;
+    TRY(hip_status(hipGetDevice(&dev), "current device"));
+    TRY(hip_status(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev), "compute unit count"));
+    TRY(hip_status(moe::launch_probe_mfma(kind, iters, cus, sink, static_cast<hipStream_t>(stream)), "probe launch"));
+    return ok();
+}
+
 }  // extern "C"

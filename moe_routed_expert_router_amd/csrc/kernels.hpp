@@ -148,9 +148,12 @@ hipError_t launch_fingerprint(const int32_t *experts, int n, const int32_t *slot
                               uint64_t *out, hipStream_t st);
 
 // Streaming read of `bytes` (a multiple of 16) from src by one launch with
-// `loads_per_thread` (4, 8 or 16) 16-byte loads per thread; writes nothing.
+// `loads_per_thread` (1, 2, 4, 8 or 16) 16-byte loads per thread; writes nothing.
 hipError_t launch_probe_read(const void *src, size_t bytes, int loads_per_thread, uint32_t *sink,
                              hipStream_t st);
+// Matrix-core rate of one MFMA kind (0 bf16, 1 fp8 x fp4, 2 fp8 x fp8, 3 fp6 x
+// fp4, 4 fp4 x fp4): 2 * cus blocks of 4 waves, iters rounds of 4 MFMAs each.
+hipError_t launch_probe_mfma(int kind, int iters, int cus, uint32_t *sink, hipStream_t st);
 
 // Host side of the manager: decayed scores and the swap rule; returns the
 // number of pairs written to pairs[2*i], pairs[2*i+1] and updates slot and score.
