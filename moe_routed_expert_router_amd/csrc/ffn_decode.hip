@@ -34,7 +34,9 @@
 // experts live, so all-resident and mixed runs still add in the same order.
 //   down + combine (T*k <= 8, one decode token): one block per 16-row tile
 //            runs every distinct expert, keeps the pairs' outputs in LDS and
-//            writes out[t] itself — no y round trip, no combine launch.
+//            writes out[t] itself — no y round trip, no combine launch; an
+//            expert's h hi and h lo rows sit in different columns of one
+//            MFMA (at most 8 pairs each), so one MFMA per K chunk, not two.
 // General kernels (any T): one wave per 16 rows.
 // Otherwise the combine kernel follows: out[t] = sum_j w[t,j] * y[t*k+j] in j
 // order, no float atomics.  (Folding the combine into a down kernel whose
@@ -384,6 +386,7 @@ __global__ __launch_bounds__(512) void ffn_down_combine(int H, int I, int T, int
                                                         const int32_t *__restrict__ ids, const float *__restrict__ w,
                                                         int out_bf16, void *__restrict__ out) {
     // P == T * k: one expert slot per pair (at most P distinct experts)
+    static_assert(P <= 8, "an expert's hi and lo columns must fit one 16-column MFMA");
     extern __shared__ __align__(16) char smem[];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
     const int nw = blockDim.x >> 6, bd = blockDim.x;
@@ -463,7 +466,8 @@ __global__ __launch_bounds__(512) void ffn_down_combine(int H, int I, int T, int
     f32x4 *red = reinterpret_cast<f32x4 *>(ls + (size_t)P * stride);   // [P][nw][64]
     int *pu = reinterpret_cast<int *>(red + (size_t)P * nw * 64);      // [P] slot of pair p (-1: none)
     int *pc = pu + P;                                                   // [P] its column in that slot's run
-    float *sw = reinterpret_cast<float *>(pc + P);                      // [P] weights (0: invalid id)
+    int *pn = pc + P;                                                   // [P] that slot's pair count
+    float *sw = reinterpret_cast<float *>(pn + P);                      // [P] weights (0: invalid id)
     float *ys = sw + P;                                                 // [P][16] pair outputs of the rows
 #pragma unroll
     for (int v = 0; v < kDcHUnits; ++v) {   // clamped units rewrite their own bytes
@@ -484,48 +488,59 @@ __global__ __launch_bounds__(512) void ffn_down_combine(int H, int I, int T, int
     }
     __syncthreads();
     if (tid < nq) {   // grouped position tid holds pair m_pl of run u
-        int u = 0, start = uo[0];
+        int u = 0, start = uo[0], end = uo[1];
 #pragma unroll
         for (int v = 1; v < P; ++v)
             if (uo[v] <= tid && v < U) {
                 u = v;
                 start = uo[v];
+                end = uo[v + 1];
             }
         pu[m_pl] = u;
         pc[m_pl] = tid - start;
+        pn[m_pl] = end - start;
     }
 
     // Every slot computes, branch-free (a masked slot multiplies zeros and
     // its sums are never read): per-slot branches let the compiler merge the
     // slots' bodies, and the merged body waits for all weights at once.
+    // A slot has n <= P <= 8 pairs, so its h hi and h lo rows share one MFMA:
+    // column c < n takes pair c's hi part, column n + c its lo part (the
+    // columns are independent; the rest read row 0 and are never used), and
+    // the two columns' sums are added after the K slices.
 #pragma unroll
     for (int u = 0; u < P; ++u) {
         const int n = uo[u + 1] - uo[u];
-        const int lo = (n > 0 ? uo[u] + (r < n ? r : 0) : 0) * stride + wave * SPW * 16 + 4 * g;
+        const bool hic = r < n;
+        const int pr = hic ? r : (r < 2 * n ? r - n : 0);
+        const uint4 *hp = (hic ? hs : ls) + (n > 0 ? uo[u] + pr : 0) * stride + wave * SPW * 16 + 4 * g;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
             float s = e8m0_to_f32((sc[u][i] >> (8 * g)) & 0xffu);
             asm volatile("" : "+v"(s));
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const bf16x8 a = fp4x8_to_bf16x8(q[u][i][m], s);
-                acc = mfma16x16x32(a, as_bf16x8(hs[lo + i * 16 + m]), acc);
-                acc = mfma16x16x32(a, as_bf16x8(ls[lo + i * 16 + m]), acc);
-            }
+            for (int m = 0; m < 4; ++m)
+                acc = mfma16x16x32(fp4x8_to_bf16x8(q[u][i][m], s), as_bf16x8(hp[i * 16 + m]), acc);
         }
         red[(u * nw + wave) * 64 + lane] = acc;
     }
     __syncthreads();
 
-    // y of pair p for row rr: its slot's K-slice partials in slice order
-    // (an invalid id or an unusable residency entry gives 0)
+    // y of pair p for row rr: its slot's K-slice partials of the hi column,
+    // then of the lo column, each in slice order (an invalid id or an
+    // unusable residency entry gives 0)
     for (int idx = tid; idx < P * 16; idx += bd) {
         const int p = idx >> 4, rr = idx & 15, u = pu[p];
         float y = 0.f;
         if (u >= 0 && ((okmask >> u) & 1u)) {
-            const int ln = pc[p] + 16 * (rr >> 2);
-            for (int s2 = 0; s2 < nw; ++s2) y += red[(u * nw + s2) * 64 + ln][rr & 3];
+            const int ln = pc[p] + 16 * (rr >> 2), ll = ln + pn[p];
+            float yh = 0.f, yl = 0.f;
+            for (int s2 = 0; s2 < nw; ++s2) {
+                yh += red[(u * nw + s2) * 64 + ln][rr & 3];
+                yl += red[(u * nw + s2) * 64 + ll][rr & 3];
+            }
+            y = yh + yl;
         }
         ys[idx] = y;
     }
@@ -838,7 +853,7 @@ size_t down_combine_lds(int T, int k, int H, int I) {
     const int P = T * k, spw = pick_spw(I / 128, 8);
     if (P > kDcMaxPairs || H % 16 != 0 || spw == 0) return 0;
     const int slices = I / 128 / spw;
-    const size_t lds = (size_t)2 * P * (I / 8 + 1) * 16 + (size_t)P * slices * 64 * 16 + (size_t)(3 + 16) * P * 4;
+    const size_t lds = (size_t)2 * P * (I / 8 + 1) * 16 + (size_t)P * slices * 64 * 16 + (size_t)(4 + 16) * P * 4;
     return lds <= kMaxLdsBytes ? lds : 0;
 }
 
