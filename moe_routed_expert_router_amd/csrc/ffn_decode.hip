@@ -18,8 +18,8 @@
 // rate), and 1 to 16 tokens per expert cost the same.
 //
 // Decode kernels (T <= 32), one 512-thread block per (row block, expert):
-//   gate/up: 8 waves = {gate, up} x RT row tiles x K slices (RT = 1 below 8
-//            tokens, 2 from 8 tokens on, so that one staging of the token
+//   gate/up: 8 waves = {gate, up} x RT row tiles x K slices (RT = 1 below 12
+//            tokens, 2 from 12 tokens on, so that one staging of the token
 //            rows serves twice the weight rows); each wave issues all of its
 //            slice's weight loads at once, before the token rows (memory-
 //            level parallelism comes from many small independent waves, not
@@ -29,7 +29,8 @@
 //            hi + lo parts (h - hi rounded again), ~16 significant bits.
 //   down:    8 waves = RT row tiles x K slices (RT = 2 below 8 tokens, else
 //            4 with the first h units requested ahead of the weights), B = h
-//            hi and h lo (two MFMAs per K slice), y[pair][row] in fp32.
+//            hi and h lo of up to 8 token rows as the 16 columns of one MFMA,
+//            y[pair][row] in fp32.
 // The block shapes depend only on T and the layer shape, never on where the
 // experts live, so all-resident and mixed runs still add in the same order.
 //   down + combine (T*k <= 8, one decode token): one block per 16-row tile
@@ -71,7 +72,12 @@ __device__ __forceinline__ void split_store_h(const f32x4 &g, const f32x4 &u, ui
 // ============================ decode block kernels ==========================
 constexpr int kStageBytes = 49152;   // LDS budget for staged tokens / h rows (3 blocks per CU)
 constexpr int kStageBytesWide = 67584;   // two-tile gate/up blocks (2 per CU by registers): 8 rows of H = 4096
-constexpr int kWideTokens = 8;       // tokens from which blocks take more weight rows
+constexpr int kWideTokens = 8;       // tokens from which down blocks take more weight rows
+// Tokens from which gate/up blocks take two row tiles (two blocks per CU by
+// registers) instead of one (three per CU).  Measured per batch-size (FFN
+// alone, Zipf routing): one tile is 3% faster at 8 tokens, even at 12, and
+// two are 3-10% faster from 16 to 32.
+constexpr int kGateUpWideTokens = 12;
 constexpr int kDmaRows = 8;          // first-pass token rows staged by LDS DMA
 
 // The distinct expert of this block for an FFN part (kPartAll / Hot / Cold)
@@ -258,8 +264,12 @@ __global__ __launch_bounds__(512) void ffn_gate_up_sel(const uint16_t *__restric
 // grid (H/(16*RT), max distinct experts of the part), 64 * RT * slices
 // threads: RT row tiles of 16 rows x slices of K.  LDS: NT rows of h hi and
 // lo and the per-wave partial sums.
+// Up to 8 steps per wave, registers are held to 80 per lane (six waves per
+// SIMD): with the LDS of 5 staged rows that is three blocks per CU instead of
+// the two that 81 registers allowed (with the shared hi / lo MFMA, the
+// batch-32 down went from 76 to 68 us).
 template <int SPW, int RT>
-__global__ __launch_bounds__(512) void ffn_down_blk(int H, int I, int NT, GroupView gv, int part,
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SPW <= 8 ? 6 : 4))) void ffn_down_blk(int H, int I, int NT, GroupView gv, int part,
                                                     const uint16_t *__restrict__ hhi,
                                                     const uint16_t *__restrict__ hlo, float *__restrict__ y) {
     extern __shared__ __align__(16) char smem[];
@@ -335,7 +345,11 @@ __global__ __launch_bounds__(512) void ffn_down_blk(int H, int I, int NT, GroupV
             __syncthreads();
         }
         const bool tv = r < nt;
-        const int lo = (tv ? r : 0) * stride + slice * SPW * 16 + 4 * g;
+        // nt <= 8: column c < nt takes row c's h hi, column nt + c its h lo,
+        // so each K chunk is one MFMA (the other columns read row 0 and are
+        // never used)
+        const int pr = tv ? r : (r < 2 * nt ? r - nt : 0);
+        const uint4 *hp = (tv ? hs : ls) + pr * stride + slice * SPW * 16 + 4 * g;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
@@ -345,23 +359,21 @@ __global__ __launch_bounds__(512) void ffn_down_blk(int H, int I, int NT, GroupV
             asm volatile("" : "+v"(s));   // keep the converts at their step
             const uint32_t w4[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const bf16x8 a = fp4x8_to_bf16x8(w4[m], s);
-                acc = mfma16x16x32(a, as_bf16x8(hs[lo + i * 16 + m]), acc);
-                acc = mfma16x16x32(a, as_bf16x8(ls[lo + i * 16 + m]), acc);
-            }
+            for (int m = 0; m < 4; ++m) acc = mfma16x16x32(fp4x8_to_bf16x8(w4[m], s), as_bf16x8(hp[i * 16 + m]), acc);
             __builtin_amdgcn_sched_barrier(0);
         }
         red[wave * 64 + lane] = acc;
         __syncthreads();
-        if (wave < RT) {   // wave rt adds its row tile's slices in a fixed order
-            f32x4 s = red[wave * 64 + lane];
-            for (int w2 = wave + RT; w2 < nw; w2 += RT) s += red[w2 * 64 + lane];
-            if (tv) {
-                const int p = gv.plist[q0 + tb + r];
-                *reinterpret_cast<float4 *>(y + (size_t)p * H + row0 + wave * 16 + 4 * g) =
-                    make_float4(s[0], s[1], s[2], s[3]);
+        if (wave < RT && tv) {   // wave rt adds its row tile's slices in a fixed order, hi then lo
+            f32x4 sh = red[wave * 64 + lane], sl = red[wave * 64 + lane + nt];
+            for (int w2 = wave + RT; w2 < nw; w2 += RT) {
+                sh += red[w2 * 64 + lane];
+                sl += red[w2 * 64 + lane + nt];
             }
+            const f32x4 s = sh + sl;
+            const int p = gv.plist[q0 + tb + r];
+            *reinterpret_cast<float4 *>(y + (size_t)p * H + row0 + wave * 16 + 4 * g) =
+                make_float4(s[0], s[1], s[2], s[3]);
         }
     }
 }
@@ -772,7 +784,7 @@ int stage_rows(int bytes_per_row, int budget = kStageBytes) {
 }
 
 // Gate/up block shape, a function of T and H only (an all-resident and a
-// mixed run of one batch then add in the same order): from kWideTokens
+// mixed run of one batch then add in the same order): from kGateUpWideTokens
 // tokens two row tiles share a block, one staging of the token rows for twice
 // the weight rows.
 struct GateUpShape {
@@ -781,7 +793,7 @@ struct GateUpShape {
 GateUpShape gate_up_shape(int T, int H) {
     const int steps = H / 128;
     GateUpShape g;
-    g.rt = (T >= kWideTokens && pick_spw(steps, 2) != 0) ? 2 : 1;
+    g.rt = (T >= kGateUpWideTokens && pick_spw(steps, 2) != 0) ? 2 : 1;
     g.spw = pick_spw(steps, 4 / g.rt);
     g.slices = g.spw ? steps / g.spw : 0;
     return g;
@@ -804,7 +816,9 @@ void launch_down_blk(const FfnArgs &a, const GroupView &gv, int part, const uint
                      float *y, int umax, hipStream_t st) {
     const int slices = a.I / 128 / SPW;
     const int row_bytes = (a.I / 8 + 1) * 16;
-    const int NT = stage_rows(2 * row_bytes);   // measured: more rows (fewer blocks per CU) is slower here
+    // measured: more rows (fewer blocks per CU) is slower here; at most 8, so
+    // that a pass's h hi and lo rows fit the 16 columns of one MFMA
+    const int NT = stage_rows(2 * row_bytes) < 8 ? stage_rows(2 * row_bytes) : 8;
     const size_t lds = (size_t)2 * NT * row_bytes + (size_t)RT * slices * 64 * 16;
     MOE_LAUNCH(part_name(part, "ffn_down_blk", "ffn_down_blk_hot", "ffn_down_blk_cold"),
                (ffn_down_blk<SPW, RT>), dim3(a.H / (16 * RT), umax), dim3(64 * RT * slices), lds, st, a.H,
