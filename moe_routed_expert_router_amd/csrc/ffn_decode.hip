@@ -9,7 +9,9 @@
 // At decode an expert sees a handful of tokens and the work is a bandwidth-
 // bound grouped GEMV over MXFP4 weights.  It still runs on the matrix cores:
 // a wave owns 16 weight rows; per 128-element K step a lane loads one 16-byte
-// run of 32 codes (exactly one MX block) and that row's block scale, turns the
+// run of 32 codes (exactly one MX block) and that row's block scale (the
+// tiled blob layout makes the wave's 16 rows of one step a contiguous 1 KB,
+// read with streaming loads), turns the
 // codes into exact bf16 with the gfx950 scaled fp4 converts, and feeds 16x16x32
 // bf16 MFMAs whose other operand holds up to 16 tokens.  The K order inside a
 // step is permuted identically in both operands (lane group g takes block
@@ -129,9 +131,9 @@ __device__ __forceinline__ void gate_up_tile_blk(const uint16_t *__restrict__ x,
     const int rt = (wave >> 1) % RT, slice = (wave >> 1) / RT;
     const int col0 = blockIdx.x * 16 * RT + rt * 16;   // first h column of this wave's tile
     const BlobLayout L = BlobLayout::make(H, I);
-    const size_t row = (size_t)role * I + col0 + r;
-    const uint8_t *qp = base + L.w13_codes + row * (H / 2) + (size_t)slice * SPW * 64 + 16 * g;
-    const uint8_t *sp = base + L.w13_scales + row * (H / 32) + (size_t)slice * SPW * 4;
+    const size_t row = (size_t)role * I + col0 + r, nst = H / 128;
+    const uint8_t *qp = base + L.w13_codes + tiled_code_row(row, nst) + (size_t)slice * SPW * kCodeStep + 16 * g;
+    const uint8_t *sp = base + L.w13_scales + tiled_scale_row(row, nst) + (size_t)slice * SPW * kScaleStep;
 
     // LDS rows in 16-byte units, padded by one unit: conflict-free token reads
     const int nch = H / 8, stride = nch + 1;
@@ -154,9 +156,9 @@ __device__ __forceinline__ void gate_up_tile_blk(const uint16_t *__restrict__ x,
     if (dma && wave < nch / 64) my_tok = pair_of(lane < ndma ? lane : ndma - 1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < SPW; ++i) q[i] = gload16(qp + (size_t)i * 64);
+    for (int i = 0; i < SPW; ++i) q[i] = gload16_nt(qp + (size_t)i * kCodeStep);
 #pragma unroll
-    for (int i = 0; i < SPW; ++i) sc[i] = gload<uint32_t>(sp + 4 * i);
+    for (int i = 0; i < SPW; ++i) sc[i] = gload_nt<uint32_t>(sp + (size_t)i * kScaleStep);
     __builtin_amdgcn_sched_barrier(0);
     if (dma && wave < nch / 64) {
         const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(x, 0xFFFFFFF0u);
@@ -290,9 +292,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SPW <= 8 ? 
         }
         return;
     }
-    const size_t row = (size_t)row0 + rt * 16 + r;
-    const uint8_t *qp = base + L.w2_codes + row * (I / 2) + (size_t)slice * SPW * 64 + 16 * g;
-    const uint8_t *sp = base + L.w2_scales + row * (I / 32) + (size_t)slice * SPW * 4;
+    const size_t row = (size_t)row0 + rt * 16 + r, nst = I / 128;
+    const uint8_t *qp = base + L.w2_codes + tiled_code_row(row, nst) + (size_t)slice * SPW * kCodeStep + 16 * g;
+    const uint8_t *sp = base + L.w2_scales + tiled_scale_row(row, nst) + (size_t)slice * SPW * kScaleStep;
     const int nch = I / 8, stride = nch + 1;   // 16-byte units per row; LDS rows padded
     uint4 *hs = reinterpret_cast<uint4 *>(smem);
     uint4 *ls = hs + (size_t)NT * stride;
@@ -318,10 +320,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SPW <= 8 ? 
     __builtin_amdgcn_sched_barrier(0);
     uint4 q[SPW];   // codes, then scales (the fills' wait counts both as outstanding)
 #pragma unroll
-    for (int i = 0; i < SPW; ++i) q[i] = gload16(qp + (size_t)i * 64);
+    for (int i = 0; i < SPW; ++i) q[i] = gload16_nt(qp + (size_t)i * kCodeStep);
     uint32_t sc[SPW];
 #pragma unroll
-    for (int i = 0; i < SPW; ++i) sc[i] = gload<uint32_t>(sp + 4 * i);
+    for (int i = 0; i < SPW; ++i) sc[i] = gload_nt<uint32_t>(sp + (size_t)i * kScaleStep);
     __builtin_amdgcn_sched_barrier(0);
 
     for (int tb = 0; tb < n; tb += NT) {
@@ -452,8 +454,9 @@ __global__ __launch_bounds__(512) void ffn_down_combine(int H, int I, int T, int
     // resource whose reads return 0), so the compiler knows how many loads
     // are in flight at every wait; scales before codes
     const uint32_t row = (uint32_t)(row0 + r);
-    const uint32_t soff = (uint32_t)L.w2_scales + row * (uint32_t)(I / 32) + (uint32_t)(wave * SPW * 4);
-    const uint32_t qoff = (uint32_t)L.w2_codes + row * (uint32_t)(I / 2) + (uint32_t)(wave * SPW * 64 + 16 * g);
+    const size_t nst = I / 128;
+    const uint32_t soff = (uint32_t)(L.w2_scales + tiled_scale_row(row, nst) + (size_t)wave * SPW * kScaleStep);
+    const uint32_t qoff = (uint32_t)(L.w2_codes + tiled_code_row(row, nst) + (size_t)wave * SPW * kCodeStep + 16 * g);
     __amdgpu_buffer_rsrc_t rs[P];
 #pragma unroll
     for (int u = 0; u < P; ++u) {
@@ -465,12 +468,12 @@ __global__ __launch_bounds__(512) void ffn_down_combine(int H, int I, int T, int
 #pragma unroll
     for (int u = 0; u < P; ++u)
 #pragma unroll
-        for (int i = 0; i < SPW; ++i) sc[u][i] = __builtin_amdgcn_raw_buffer_load_b32(rs[u], soff + 4 * i, 0, 0);
+        for (int i = 0; i < SPW; ++i) sc[u][i] = __builtin_amdgcn_raw_buffer_load_b32(rs[u], soff + (uint32_t)kScaleStep * i, 0, kLoadNT);
 #pragma unroll
     for (int u = 0; u < P; ++u)
 #pragma unroll
         for (int i = 0; i < SPW; ++i)
-            q[u][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs[u], qoff + 64 * i, 0, 0));
+            q[u][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs[u], qoff + (uint32_t)kCodeStep * i, 0, kLoadNT));
     __builtin_amdgcn_sched_barrier(0);
 
     uint4 *hs = reinterpret_cast<uint4 *>(smem);
@@ -579,16 +582,16 @@ struct GateUpStage {
 
 template <int D>
 __device__ __forceinline__ void gate_up_load(GateUpStage<D> &st, const uint8_t *gq, const uint8_t *uq,
-                                             const uint32_t *gs, const uint32_t *us, const uint16_t *xr,
+                                             const uint8_t *gs, const uint8_t *us, const uint16_t *xr,
                                              bool tv, int s0) {
     const uint4 z4 = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int d = 0; d < D; ++d) {
         const int s = s0 + d;
-        st.gq[d] = *reinterpret_cast<const uint4 *>(gq + (size_t)s * 64);
-        st.uq[d] = *reinterpret_cast<const uint4 *>(uq + (size_t)s * 64);
-        st.gs[d] = gs[s];
-        st.us[d] = us[s];
+        st.gq[d] = *reinterpret_cast<const uint4 *>(gq + (size_t)s * kCodeStep);
+        st.uq[d] = *reinterpret_cast<const uint4 *>(uq + (size_t)s * kCodeStep);
+        st.gs[d] = *reinterpret_cast<const uint32_t *>(gs + (size_t)s * kScaleStep);
+        st.us[d] = *reinterpret_cast<const uint32_t *>(us + (size_t)s * kScaleStep);
 #pragma unroll
         for (int m = 0; m < 4; ++m)
             st.xb[d][m] = tv ? *reinterpret_cast<const uint4 *>(xr + (size_t)s * 128 + 8 * m) : z4;
@@ -625,11 +628,11 @@ __global__ __launch_bounds__(64) void ffn_gate_up_wave(const uint16_t *__restric
     const int lane = threadIdx.x, r = lane & 15, g = lane >> 4;
     const int row = blockIdx.x * 16 + r;
     const BlobLayout L = BlobLayout::make(H, I);
-    const size_t rb = (size_t)H / 2, sb = (size_t)H / 32;
-    const uint8_t *gq = base + L.w13_codes + (size_t)row * rb + 16 * g;
-    const uint8_t *uq = gq + (size_t)I * rb;
-    const uint32_t *gs = reinterpret_cast<const uint32_t *>(base + L.w13_scales + (size_t)row * sb);
-    const uint32_t *us = reinterpret_cast<const uint32_t *>(base + L.w13_scales + (size_t)(I + row) * sb);
+    const size_t nst = H / 128;
+    const uint8_t *gq = base + L.w13_codes + tiled_code_row(row, nst) + 16 * g;
+    const uint8_t *uq = base + L.w13_codes + tiled_code_row((size_t)I + row, nst) + 16 * g;
+    const uint8_t *gs = base + L.w13_scales + tiled_scale_row(row, nst);
+    const uint8_t *us = base + L.w13_scales + tiled_scale_row((size_t)I + row, nst);
     const int nsteps = H / 128;
     for (int tb = 0; tb < n; tb += 16) {
         const bool tv = tb + r < n;   // this lane's token column is r
@@ -661,14 +664,14 @@ struct DownStage {
 };
 
 template <int D>
-__device__ __forceinline__ void down_load(DownStage<D> &st, const uint8_t *wq, const uint32_t *ws,
+__device__ __forceinline__ void down_load(DownStage<D> &st, const uint8_t *wq, const uint8_t *ws,
                                           const uint16_t *hh, const uint16_t *hl, bool tv, int s0) {
     const uint4 z4 = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int d = 0; d < D; ++d) {
         const int s = s0 + d;
-        st.wq[d] = *reinterpret_cast<const uint4 *>(wq + (size_t)s * 64);
-        st.ws[d] = ws[s];
+        st.wq[d] = *reinterpret_cast<const uint4 *>(wq + (size_t)s * kCodeStep);
+        st.ws[d] = *reinterpret_cast<const uint32_t *>(ws + (size_t)s * kScaleStep);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             st.hh[d][m] = tv ? *reinterpret_cast<const uint4 *>(hh + (size_t)s * 128 + 8 * m) : z4;
@@ -712,8 +715,9 @@ __global__ __launch_bounds__(64) void ffn_down_wave(int H, int I, GroupView gv, 
     }
     const BlobLayout L = BlobLayout::make(H, I);
     const int row = row0 + r;
-    const uint8_t *wq = base + L.w2_codes + (size_t)row * (I / 2) + 16 * g;
-    const uint32_t *ws = reinterpret_cast<const uint32_t *>(base + L.w2_scales + (size_t)row * (I / 32));
+    const size_t nst = I / 128;
+    const uint8_t *wq = base + L.w2_codes + tiled_code_row(row, nst) + 16 * g;
+    const uint8_t *ws = base + L.w2_scales + tiled_scale_row(row, nst);
     const int nsteps = I / 128;
     for (int tb = 0; tb < n; tb += 16) {
         const bool tv = tb + r < n;

@@ -144,17 +144,18 @@ __device__ __forceinline__ void gate_up_tile(__amdgpu_buffer_rsrc_t xrs, int H, 
         const int c = 4 * (wave * T5 + j) + (lane >> 4), chunk = (lane & 15) ^ (c & 15);
         xsrc[j] = ((uint32_t)(gv.plist[t.q0 + (c < t.nt ? c : 0)] / k) * (uint32_t)H + chunk * 8) * 2;
     }
+    const size_t nst = H / 128;   // tiled blob: one 16-row group's step is 1 KB of codes, 64 B of scales
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {    // weight rows 16 (4w + j) .. +15, four lanes per row
+    for (int j = 0; j < 4; ++j) {    // weight rows 16 (4w + j) .. +15 (one tile: 1 KB contiguous), four lanes per row
         const int r = 16 * (4 * wave + j) + (lane >> 2), chunk = (lane & 3) ^ ((r >> 2) & 3);
-        const uint32_t row = (uint32_t)((r >> 8) * I + t.rb * 256 + (r & 255));
-        wsrc[j] = (uint32_t)L.w13_codes + row * (uint32_t)(H / 2) + 16 * chunk;
+        const size_t row = (size_t)((r >> 8) * I + t.rb * 256 + (r & 255));
+        wsrc[j] = (uint32_t)(L.w13_codes + tiled_code_row(row, nst)) + 16 * chunk;
     }
     uint32_t ssrc;
     {                                // scales of weight rows 64 w .. +63, one per lane
         const int r = 64 * wave + lane;
-        const uint32_t row = (uint32_t)((r >> 8) * I + t.rb * 256 + (r & 255));
-        ssrc = (uint32_t)L.w13_scales + row * (uint32_t)(H / 32);
+        const size_t row = (size_t)((r >> 8) * I + t.rb * 256 + (r & 255));
+        ssrc = (uint32_t)(L.w13_scales + tiled_scale_row(row, nst));
     }
     // reads of this wave: operand f row r_f = 256 f + 32 w + lc
     int wro[2][2], sro[2];
@@ -165,16 +166,19 @@ __device__ __forceinline__ void gate_up_tile(__amdgpu_buffer_rsrc_t xrs, int H, 
         for (int q = 0; q < 2; ++q) wro[f][q] = kGuW + r * 64 + 16 * ((2 * h + q) ^ ((r >> 2) & 3));
         sro[f] = kGuS + 4 * r;
     }
-    int roff[8];   // sub-step m: chunk 8h + m of token row lc (column tile b adds 32 rows)
-#pragma unroll
-    for (int m = 0; m < 8; ++m) roff[m] = lc * 256 + 16 * ((8 * h + m) ^ (lc & 15));
+    // sub-step m reads chunk 8h + m of token row lc (column tile b adds 32
+    // rows): slot (8h + m) ^ (lc & 15) = (8h ^ (lc & 8)) + (m ^ (lc & 7)), so
+    // two registers give all eight offsets (eight would spill a fill address,
+    // and its reload in the K loop would wait for that step's fills)
+    const int rbase = lc * 256 + 16 * ((8 * h) ^ (lc & 8)), rx = lc & 7;
 
     auto fill = [&](uint8_t *st, int nx) {
 #pragma unroll
         for (int j = 0; j < T5; ++j) lds_fill<16>(xrs, xsrc[j] + nx * 256, st + (wave * T5 + j) * 1024);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) lds_fill<16>(wrs, wsrc[j] + nx * 64, st + kGuW + (4 * wave + j) * 1024);
-        lds_fill<4>(wrs, ssrc + nx * 4, st + kGuS + wave * 256);
+        for (int j = 0; j < 4; ++j)
+            lds_fill<16>(wrs, wsrc[j] + nx * (uint32_t)kCodeStep, st + kGuW + (4 * wave + j) * 1024);
+        lds_fill<4>(wrs, ssrc + nx * (uint32_t)kScaleStep, st + kGuS + wave * 256);
     };
 
     f32x16 acc[2][kCT];
@@ -199,10 +203,13 @@ __device__ __forceinline__ void gate_up_tile(__amdgpu_buffer_rsrc_t xrs, int H, 
             }
         }
         constexpr int U = 8 * T5;    // units (m, b): m = u / T5, b = u % T5
+        int rxs = rx;                // opaque per step, so the eight offsets are not hoisted into registers
+        asm volatile("" : "+v"(rxs));
         bf16x8 bq[U];
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            bq[u] = __builtin_bit_cast(bf16x8, lds_ld<u32x4>(cur + roff[u / T5] + (u % T5) * 32 * 256));
+            bq[u] = __builtin_bit_cast(bf16x8,
+                                       lds_ld<u32x4>(cur + rbase + 16 * ((u / T5) ^ rxs) + (u % T5) * 32 * 256));
         bf16x8 a[2];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -286,12 +293,13 @@ __device__ __forceinline__ void down_tile(int H, int I, uint32_t plane, const Gr
         const int c = 4 * (wave * T5 + j) + (lane >> 4), chunk = (lane & 15) ^ (c & 15);
         xsrc[j] = ((chunk < 8 ? 0u : plane) + (uint32_t)(t.q0 + (c < t.nt ? c : 0)) * (uint32_t)I + (chunk & 7) * 8) * 2;
     }
+    const size_t nst = I / 128;   // tiled blob: a 64-K step is one half of each row's 64 bytes of a tile
 #pragma unroll
     for (int j = 0; j < 2; ++j) {    // weight rows 32 (2w + j) .. +31, two lanes per row
         const int r = 32 * (2 * wave + j) + (lane >> 1), chunk = (lane & 1) ^ ((r >> 3) & 1);
-        wsrc[j] = (uint32_t)L.w2_codes + (orow0 + r) * (uint32_t)(I / 2) + 16 * chunk;
+        wsrc[j] = (uint32_t)(L.w2_codes + tiled_code_row(orow0 + r, nst)) + 16 * chunk;
     }
-    const uint32_t ssrc = (uint32_t)L.w2_scales + (orow0 + 64 * wave + lane) * (uint32_t)(I / 32);
+    const uint32_t ssrc = (uint32_t)(L.w2_scales + tiled_scale_row(orow0 + 64 * wave + lane, nst));
     int wro[2], sro[2];
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
@@ -306,9 +314,10 @@ __device__ __forceinline__ void down_tile(int H, int I, uint32_t plane, const Gr
     auto fill = [&](uint8_t *st, int nx) {
 #pragma unroll
         for (int j = 0; j < T5; ++j) lds_fill<16>(hrs, xsrc[j] + nx * 128, st + (wave * T5 + j) * 1024);
+        const uint32_t wstep = (uint32_t)(nx >> 1) * (uint32_t)kCodeStep + (uint32_t)(nx & 1) * 32;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) lds_fill<16>(wrs, wsrc[j] + nx * 32, st + kDnW + (2 * wave + j) * 1024);
-        lds_fill<4>(wrs, ssrc + (nx >> 1) * 4, st + kDnS + wave * 256);
+        for (int j = 0; j < 2; ++j) lds_fill<16>(wrs, wsrc[j] + wstep, st + kDnW + (2 * wave + j) * 1024);
+        lds_fill<4>(wrs, ssrc + (uint32_t)(nx >> 1) * (uint32_t)kScaleStep, st + kDnS + wave * 256);
     };
 
     f32x16 acc[2][kCT];

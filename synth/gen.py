@@ -97,13 +97,15 @@ def workload(name: str) -> Workload:
 
 
 # --------------------------------------------------------------------------
-# Expert blob layout (a stated convention; the oracle and the HIP library
-# each read it with their own code).  One contiguous blob per expert:
-#   w13 nibbles [2I][H/2] u8   rows 0..I-1 gate (w1), rows I..2I-1 up (w3)
-#   w13 scales  [2I][H/32] u8  e8m0, one per 32 elements along H
-#   w2  nibbles [H][I/2]  u8   down projection, contraction along I
-#   w2  scales  [H][I/32] u8
-# Two e2m1 codes per byte, the even element in the low nibble.
+# Expert blob sections (a stated convention; the oracle and the HIP library
+# each read the bytes with their own code).  One contiguous blob per expert,
+# four sections in this order, each filled as one keyed byte stream:
+#   w13 codes   2I*H/2 bytes   e2m1, two per byte (gate rows, then up rows)
+#   w13 scales  2I*H/32 bytes  e8m0, one per 32 elements along H
+#   w2  codes   H*I/2 bytes    down projection, contraction along I
+#   w2  scales  H*I/32 bytes
+# Where a given (row, column) sits inside a section is the readers' layout
+# (tiles of 16 rows x 128 columns); the generator only fills bytes.
 # --------------------------------------------------------------------------
 def section_sizes(H: int, I: int) -> tuple[int, int, int, int]:
     return (2 * I * H // 2, 2 * I * H // 32, H * I // 2, H * I // 32)
@@ -164,28 +166,22 @@ def _scale_bytes_from_words(w: np.ndarray) -> np.ndarray:
 
 
 def expert_sections(seed: int, layer: int, expert: int, H: int, I: int):
-    """(w13_nibbles [2I][H/2], w13_scales [2I][H/32], w2_nibbles [H][I/2],
-    w2_scales [H][I/32]) as uint8 arrays for one expert."""
-    n13, s13, n2, s2 = section_sizes(H, I)
+    """The four section byte streams (w13 codes, w13 scales, w2 codes, w2
+    scales) of one expert, as flat uint8 arrays in blob order."""
     out = []
-    for tag, nbytes, shape in (
-        (TAG_W13_NIB, n13, (2 * I, H // 2)),
-        (TAG_W13_SCALE, s13, (2 * I, H // 32)),
-        (TAG_W2_NIB, n2, (H, I // 2)),
-        (TAG_W2_SCALE, s2, (H, I // 32)),
-    ):
+    for tag, nbytes in zip((TAG_W13_NIB, TAG_W13_SCALE, TAG_W2_NIB, TAG_W2_SCALE), section_sizes(H, I)):
         k1, k2 = stream_keys(seed, tag, layer, expert)
         if tag in (TAG_W13_NIB, TAG_W2_NIB):
             w = hash_words_np(k1, k2, nbytes // 4)
             b = w.astype("<u4").view(np.uint8)
         else:
             b = _scale_bytes_from_words(hash_words_np(k1, k2, nbytes))
-        out.append(b.reshape(shape))
+        out.append(b)
     return tuple(out)
 
 
 def expert_blob(seed: int, layer: int, expert: int, H: int, I: int) -> np.ndarray:
-    return np.concatenate([s.reshape(-1) for s in expert_sections(seed, layer, expert, H, I)])
+    return np.concatenate(expert_sections(seed, layer, expert, H, I))
 
 
 # ---------------------------- GPU-side generation ---------------------------

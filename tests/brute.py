@@ -43,7 +43,8 @@ def bf16_value(bits):
 
 def weight(blob, H, I, plane, r, c):
     """Dequantised element (row r, column c) of plane 'w13' ([2I][H]) or 'w2'
-    ([H][I]), read byte by byte from the expert blob."""
+    ([H][I]), read byte by byte from the expert blob (planes in tiles of 16
+    rows x 128 columns: 1 KB of codes and 64 B of scales per tile)."""
     n13 = 2 * I * H // 2
     s13 = 2 * I * H // 32
     n2 = H * I // 2
@@ -51,9 +52,10 @@ def weight(blob, H, I, plane, r, c):
         K, nib_off, sc_off = H, 0, n13
     else:
         K, nib_off, sc_off = I, n13 + s13, n13 + s13 + n2
-    byte = int(blob[nib_off + r * (K // 2) + c // 2])
+    tile = (r // 16) * (K // 128) + c // 128
+    byte = int(blob[nib_off + tile * 1024 + (r % 16) * 64 + (c % 128) // 2])
     code = (byte >> 4) if (c % 2) else (byte & 0xF)
-    sbyte = int(blob[sc_off + r * (K // 32) + c // 32])
+    sbyte = int(blob[sc_off + tile * 64 + (r % 16) * 4 + (c % 128) // 32])
     if sbyte == 255:
         return float("nan")
     return math.ldexp(E2M1[code], sbyte - 127)

@@ -49,10 +49,12 @@ def _zero_blob():
 
 
 def _set_scales(b, value_fn):
+    """b with every scale byte (row, block) set to value_fn((row, block))."""
     w13q, w13s, w2q, w2s = blob.split(b, H, I)
     for arr in (w13s, w2s):
         for idx in np.ndindex(arr.shape):
             arr[idx] = value_fn(idx)
+    return blob.join(w13q, w13s, w2q, w2s)
 
 
 def _put(codes_view, r, c, code):
@@ -65,9 +67,8 @@ def _put(codes_view, r, c, code):
 
 
 def test_all_zero_codes_give_zero():
-    b = _zero_blob()
     rng = np.random.default_rng(0)
-    _set_scales(b, lambda idx: int(rng.integers(100, 140)))
+    b = _set_scales(_zero_blob(), lambda idx: int(rng.integers(100, 140)))
     w13, w2 = blob.weights(b, H, I)
     x = route.bf16_bits_to_f32(gen.tokens_bf16(0, 0, T, H))
     y = ffn.expert_ffn(x, w13, w2)
@@ -76,8 +77,7 @@ def test_all_zero_codes_give_zero():
 
 def test_one_nonzero_per_row_closed_form():
     rng = np.random.default_rng(1)
-    b = _zero_blob()
-    _set_scales(b, lambda idx: 127)
+    b = _set_scales(_zero_blob(), lambda idx: 127)
     w13q, w13s, w2q, w2s = blob.split(b, H, I)
     a = rng.integers(0, H, I)           # gate row j reads x[a_j]
     bb = rng.integers(0, H, I)          # up row j reads x[b_j]
@@ -93,6 +93,7 @@ def test_one_nonzero_per_row_closed_form():
     for r in range(H):
         _put(w2q, r, c[r], 2)
         w2s[r, c[r] // 32] = s2[r]
+    b = blob.join(w13q, w13s, w2q, w2s)
     w13, w2 = blob.weights(b, H, I)
     xb = gen.tokens_bf16(3, 0, T, H)
     x = route.bf16_bits_to_f32(xb).astype(np.float64)
@@ -110,9 +111,8 @@ def test_one_nonzero_per_row_closed_form():
 def test_w2_scale_plus_one_doubles_exactly():
     x, wr, blobs = _inputs(1)
     b0 = blobs[3]
-    b1 = b0.copy()
-    _, _, _, w2s = blob.split(b1, H, I)
-    w2s += 1
+    w13q, w13s, w2q, w2s = blob.split(b0, H, I)
+    b1 = blob.join(w13q, w13s, w2q, w2s + 1)
     xf = route.bf16_bits_to_f32(x)
     y0 = ffn.expert_ffn(xf, *blob.weights(b0, H, I))
     y1 = ffn.expert_ffn(xf, *blob.weights(b1, H, I))

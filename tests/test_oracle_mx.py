@@ -95,12 +95,39 @@ def test_blob_sizes(H, I, expect):
     assert blob.blob_bytes(H, I) == expect[4] == 3 * H * I * 17 // 32
 
 
-def test_blob_split_matches_generator_sections():
+def test_blob_split_reads_the_tiled_layout_by_brute_force():
+    """Every code and scale of split() against the tile formula evaluated
+    element by element on the generator's section streams (16-row x
+    128-column tiles; 1 KB of codes and 64 B of scales per tile)."""
     H, I = 256, 128
     secs = gen.expert_sections(7, 2, 5, H, I)
     b = gen.expert_blob(7, 2, 5, H, I)
-    for got, want in zip(blob.split(b, H, I), secs):
-        assert got.shape == want.shape and np.array_equal(got, want)
+    got = blob.split(b, H, I)
+    for plane, (R, K) in ((0, (2 * I, H)), (1, (H, I))):
+        codes, scales = got[2 * plane], got[2 * plane + 1]
+        csec, ssec = secs[2 * plane], secs[2 * plane + 1]
+        assert codes.shape == (R, K // 2) and scales.shape == (R, K // 32)
+        nst = K // 128
+        for r in range(R):
+            for cb in range(K // 2):          # code byte cb holds columns 2cb, 2cb+1
+                tile = (r // 16) * nst + (2 * cb) // 128
+                assert codes[r, cb] == csec[tile * 1024 + (r % 16) * 64 + cb % 64]
+            for sb in range(K // 32):
+                tile = (r // 16) * nst + sb // 4
+                assert scales[r, sb] == ssec[tile * 64 + (r % 16) * 4 + sb % 4]
+
+
+def test_blob_join_inverts_split():
+    H, I = 384, 256
+    b = gen.expert_blob(3, 1, 2, H, I)
+    assert np.array_equal(blob.join(*blob.split(b, H, I)), b)
+    # and a planted byte lands where the layout says: row 21, code byte 70 of w2
+    w13q, w13s, w2q, w2s = blob.split(b, H, I)
+    w2q[21, 70] ^= 0xFF
+    b2 = blob.join(w13q, w13s, w2q, w2s)
+    diff = np.flatnonzero(b2 != b)
+    off = sum(blob.sizes(H, I)[:2]) + ((21 // 16) * (I // 128) + 70 // 64) * 1024 + (21 % 16) * 64 + 70 % 64
+    assert diff.tolist() == [off]
 
 
 def test_generator_scale_bytes_in_range():
