@@ -40,10 +40,15 @@
  *     expert; MXFP4: FP4 E2M1 codes, two per byte with the even element in the
  *     low nibble, and one E8M0 scale per 32 consecutive elements along the
  *     contraction axis, following the OCP MX v1.0 formats):
- *         w13 codes  [2I][H/2]   rows 0..I-1 gate (w1), rows I..2I-1 up (w3)
- *         w13 scales [2I][H/32]
- *         w2  codes  [H][I/2]    down projection
- *         w2  scales [H][I/32]
+ *         w13 codes  (2I x H)   rows 0..I-1 gate (w1), rows I..2I-1 up (w3)
+ *         w13 scales
+ *         w2  codes  (H x I)    down projection
+ *         w2  scales
+ *     in that order, each plane of R rows and K columns stored in tiles of
+ *     16 rows x 128 columns (nst = K/128): the codes of row r, column c are
+ *     byte ((r/16)*nst + c/128)*1024 + (r%16)*64 + (c%128)/2 of the plane's
+ *     codes section, and the scale of row r, block b = c/32 is byte
+ *     ((r/16)*nst + b/4)*64 + (r%16)*4 + b%4 of its scales section.
  *   - Residency table slot[E] (int32): slot[e] >= 0 means expert e is hot and
  *     lives at hot_base + slot[e]*B; slot[e] < 0 means cold, with cold index
  *     c = -slot[e]-1: its bytes are at host_cold + c*B and it runs from
