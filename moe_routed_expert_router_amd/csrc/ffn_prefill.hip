@@ -16,9 +16,12 @@
 // then reads its weight codes from LDS, converts them once per MFMA sub-step
 // and runs the MFMAs, with the token operand reads issued a few MFMAs ahead.
 // gate/up: operand 0 = 32 gate rows, operand 1 = the matching 32 up rows (a
-// block covers 256 columns of h); the epilogue stores h = silu(g) * u as bf16
-// hi + lo parts.  down: two 32-row operands of W2 (a block covers 512 output
-// rows); h hi and lo both feed the same accumulators.
+// block covers 256 columns of h); the epilogue stores h = silu(g) * u as a
+// bf16 hi part and the remainder lo as MXFP8 (e4m3 codes, one e8m0 scale per
+// 32 columns).  down: two 32-row operands of W2 (a block covers 512 output
+// rows); h hi enters bf16 MFMAs on the converted weights, h lo one scaled
+// fp4 x fp8 MFMA per K step on the weight codes as stored, both into the same
+// accumulators.
 //
 // K permutation: inside one K step, lane half h (lanes 32h..32h+31) covers a
 // contiguous run of K made of whole MX blocks, and MFMA sub-step m takes the
@@ -68,6 +71,35 @@ __device__ __forceinline__ T lds_ld(const uint8_t *p) {
     return *reinterpret_cast<const T *>(p);
 }
 
+// Least e with amax <= 448 * 2^e (448: the largest e4m3 value), clamped to
+// e8m0's [-127, 127]; -127 for amax = 0.
+__device__ __forceinline__ int e8m0_for(float amax) {
+    if (!(amax > 0.f)) return -127;
+    int e = (int)((__float_as_uint(amax) >> 23) & 255u) - 127 - 8;   // amax / 2^e in [256, 512)
+    if (amax > ldexpf(448.f, e)) ++e;
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Four values as e4m3 codes (round to nearest even), a in the low byte.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+    const uint32_t v = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)v, true);
+}
+
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+// D += W x H over one 64-K step on the scaled 32x32x64 MFMA: A = 32 weight
+// rows as fp4 codes (lane half h: K [32h, 32h+32), element order) with their
+// e8m0 scale bytes, B = 32 token columns as e4m3 codes (lane half h: K [16h,
+// 16h+16) in xa, [32+16h, 32+16h+16) in xb) with theirs; lane half h's
+// scale covers K block h for both operands.
+__device__ __forceinline__ f32x16 mfma_f4_f8(const u32x4 &w, const u32x4 &xa, const u32x4 &xb, uint32_t ws,
+                                             uint32_t xs, f32x16 c) {
+    const i32x8 a = {(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+    const i32x8 b = {(int)xa[0], (int)xa[1], (int)xa[2], (int)xa[3], (int)xb[0], (int)xb[1], (int)xb[2], (int)xb[3]};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 0, 0, (int)ws, 0, (int)xs);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -110,6 +142,31 @@ __device__ __forceinline__ void pipeline_order() {
         __builtin_amdgcn_sched_group_barrier(0x008, MPU, 0);                       // MFMA
         if (u + kAhead < U) __builtin_amdgcn_sched_group_barrier(0x100, RPU, 0);   // DS read
     }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// The down step's order: its T5 + 3 fills, the weight and scale reads
+// (4 + T5) and the operand reads of the first kAhead units, then per unit its
+// two MFMAs and the reads of the unit kAhead later (one for a hi unit, two
+// for a lo unit; the 4 T5 hi units come first).
+template <int T5>
+__device__ __forceinline__ void pipeline_order_down() {
+    static_assert(kAhead == 2 && 4 * T5 > kAhead, "unit counts below assume two units ahead");
+    constexpr int UH = 4 * T5, U = UH + T5;
+    __builtin_amdgcn_sched_group_barrier(0x020, T5 + 3, 0);          // VMEM (LDS fills)
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 + T5 + kAhead, 0); // DS reads
+#pragma unroll
+    for (int u = 0; u < UH - kAhead; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int u = UH - kAhead; u < U - kAhead; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+#pragma unroll
+    for (int u = U - kAhead; u < U; ++u) __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -224,25 +281,44 @@ __device__ __forceinline__ void gate_up_tile(__amdgpu_buffer_rsrc_t xrs, int H, 
         pipeline_order<U, T5 + 5, 6, 1, 2>();
     });
 
-    // lane (lc, h), element i: h column hcol + 8 (i / 4) + 4h + i % 4, token column 32 b + lc
+    // lane (lc, h), element i: h column hcol + 8 (i / 4) + 4h + i % 4, token
+    // column 32 b + lc.  The wave's 32 columns are one MX block of h along I,
+    // half in each lane half.  h = hi + lo: hi is h rounded to bf16, lo = h -
+    // hi (exact in fp32) is stored as e4m3 codes under one e8m0 scale per
+    // (token, block), the least power of two that puts the block's largest
+    // |lo| at or below 448.  Lo plane (bytes from hlo): codes [P][I], then
+    // scale slots [P][I/64][16] (bytes 0 and 1 of a slot: the two blocks of
+    // a 64-column step).
     const size_t hcol = (size_t)t.rb * 256 + 32 * wave;
+    const size_t plane = (size_t)(hlo - hhi);
+    uint8_t *lq = reinterpret_cast<uint8_t *>(hlo);
+    uint8_t *ls = lq + plane;
 #pragma unroll
     for (int b = 0; b < T5; ++b) {
         const int c = 32 * b + lc;
+        uint32_t hi[16];
+        float r[16], amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float v = silu(acc[0][b][i]) * acc[1][b][i];
+            hi[i] = f32_to_bf16_bits(v);
+            r[i] = v - __uint_as_float(hi[i] << 16);
+            amax = fmaxf(amax, fabsf(r[i]));
+        }
+        amax = fmaxf(amax, __shfl_xor(amax, 32));   // the block's other 16 columns
+        const int e = e8m0_for(amax);
+        const float inv = ldexpf(1.f, -e);
         if (c < t.nt) {
+            const size_t row = (size_t)(t.q0 + c);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                uint32_t hi[4], lo[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float v = silu(acc[0][b][4 * j + i]) * acc[1][b][4 * j + i];
-                    hi[i] = f32_to_bf16_bits(v);
-                    lo[i] = f32_to_bf16_bits(v - __uint_as_float(hi[i] << 16));
-                }
-                const size_t off = (size_t)(t.q0 + c) * I + hcol + 8 * j + 4 * h;
-                *reinterpret_cast<uint2 *>(hhi + off) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
-                *reinterpret_cast<uint2 *>(hlo + off) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+                const size_t off = row * I + hcol + 8 * j + 4 * h;
+                *reinterpret_cast<uint2 *>(hhi + off) =
+                    make_uint2(hi[4 * j] | (hi[4 * j + 1] << 16), hi[4 * j + 2] | (hi[4 * j + 3] << 16));
+                *reinterpret_cast<uint32_t *>(lq + off) =
+                    e4m3x4(r[4 * j] * inv, r[4 * j + 1] * inv, r[4 * j + 2] * inv, r[4 * j + 3] * inv);
             }
+            if (h == 0) ls[(row * (I / 64) + hcol / 64) * 16 + (wave & 1)] = (uint8_t)(e + 127);
         }
     }
 }
@@ -266,11 +342,15 @@ __global__ __launch_bounds__(kThreads) void ffn_gate_up_gemm(const uint16_t *__r
 }
 
 // ---------------------------------------------------------------------------
-// down: K step 64.  Lane half h covers K [32h, 32h+32) of the step (MX block
-// h); sub-step m = 0..3 takes its elements 8m..8m+7.
-// Stage: h tile (a row holds h hi in chunks 0..7 and h lo in chunks 8..15 for
-// the step's 64 K) | W2 codes [512 rows][32 B] | scales [512 rows][4 B] (the
-// aligned dword holding the step's two scale bytes and those of its pair
+// down: K step 64.  Lane half h holds K [32h, 32h+32) of the step (MX block
+// h) of its W2 row; h hi enters four bf16 MFMAs (sub-step m = 0..3 takes
+// elements 8m..8m+7, the token operand read with the same permutation) and h
+// lo one scaled fp4 x fp8 MFMA on the same W2 codes, as stored, with their
+// scale bytes.
+// Stage: h tile (a row holds, for the step's 64 K, h hi in chunks 0..7, the
+// e4m3 codes of h lo in chunks 8..11 and its scale slot in chunk 12; chunks
+// 13..15 are not filled) | W2 codes [512 rows][32 B] | scales [512 rows][4 B]
+// (the aligned dword holding the step's two scale bytes and those of its pair
 // step); weight row r = 64 w + 32 f + c holds its 2 chunks in slots
 // k ^ ((r >> 3) & 1).
 // grid: 8-aligned (H/512 row blocks x token tiles); 512 threads.
@@ -287,12 +367,32 @@ __device__ __forceinline__ void down_tile(int H, int I, uint32_t plane, const Gr
     const BlobLayout L = BlobLayout::make(H, I);
     const __amdgpu_buffer_rsrc_t wrs = buffer_rsrc(t.base, (uint32_t)L.bytes);
     const uint32_t orow0 = (uint32_t)t.rb * 512;
-    uint32_t xsrc[T5], wsrc[2];
+    // h rows 4 (w T5 + j) .. +3.  hbuf bytes: hi [P][I] bf16 from 0, lo codes
+    // [P][I] from 2 plane, lo scale slots [P][I/64][16] from 3 plane.  A
+    // fill's step offset is nx * 128 >> shift: shift 0 for hi, 1 for lo codes,
+    // 3 for the scale slot; xsh holds 2 bits per fill.  Chunks 13..15 take an
+    // offset past the buffer's end (kNoFill + at most 16 I / 64 < 2^32), where
+    // a buffer load reads nothing and returns zeros: no branch in the K loop.
+    constexpr uint32_t kNoFill = 0x80000000u;
+    uint32_t xsrc[T5], xsh = 0;
 #pragma unroll
-    for (int j = 0; j < T5; ++j) {   // h rows 4 (w T5 + j) .. +3 (lo plane `plane` elements after hi)
+    for (int j = 0; j < T5; ++j) {
         const int c = 4 * (wave * T5 + j) + (lane >> 4), chunk = (lane & 15) ^ (c & 15);
-        xsrc[j] = ((chunk < 8 ? 0u : plane) + (uint32_t)(t.q0 + (c < t.nt ? c : 0)) * (uint32_t)I + (chunk & 7) * 8) * 2;
+        const uint32_t row = (uint32_t)(t.q0 + (c < t.nt ? c : 0));
+        uint32_t sh;
+        if (chunk < 8) {
+            xsrc[j] = (row * (uint32_t)I + chunk * 8) * 2;
+            sh = 0;
+        } else if (chunk < 12) {
+            xsrc[j] = 2 * plane + row * (uint32_t)I + (chunk - 8) * 16;
+            sh = 1;
+        } else {
+            xsrc[j] = chunk == 12 ? 3 * plane + row * (uint32_t)(I / 4) : kNoFill;
+            sh = 3;
+        }
+        xsh |= sh << (2 * j);
     }
+    uint32_t wsrc[2];
     const size_t nst = I / 128;   // tiled blob: a 64-K step is one half of each row's 64 bytes of a tile
 #pragma unroll
     for (int j = 0; j < 2; ++j) {    // weight rows 32 (2w + j) .. +31, two lanes per row
@@ -307,13 +407,19 @@ __device__ __forceinline__ void down_tile(int H, int I, uint32_t plane, const Gr
         wro[f] = kDnW + r * 32 + 16 * (h ^ ((r >> 3) & 1));
         sro[f] = kDnS + 4 * r + h;   // + 2 for odd steps
     }
-    int roff[8];   // hi: chunk 4h + m (roff[m]); lo: chunk 8 + 4h + m (roff[4 + m])
-#pragma unroll
-    for (int i = 0; i < 8; ++i) roff[i] = lc * 256 + 16 * ((8 * (i >> 2) + 4 * h + (i & 3)) ^ (lc & 15));
+    // token row lc (column tile b adds 32 rows): hi chunk 4h + m in slot
+    // (4h ^ (lc & 12)) + (m ^ (lc & 3)); lo chunk 8 + 2q + h in slot
+    // ((8 + h) ^ (lc & 13)) + 2 (q ^ ((lc >> 1) & 1)); scale byte h of chunk
+    // 12.  Two registers each give the hi and lo offsets (made opaque per
+    // step, so the six offsets are not hoisted into registers).
+    const int rbase = lc * 256 + 16 * ((4 * h) ^ (lc & 12)), rx = lc & 3;
+    const int lbase = lc * 256 + 16 * ((8 + h) ^ (lc & 13)), lx = (lc >> 1) & 1;
+    const int soff = lc * 256 + 16 * (12 ^ (lc & 15)) + h;
 
     auto fill = [&](uint8_t *st, int nx) {
 #pragma unroll
-        for (int j = 0; j < T5; ++j) lds_fill<16>(hrs, xsrc[j] + nx * 128, st + (wave * T5 + j) * 1024);
+        for (int j = 0; j < T5; ++j)
+            lds_fill<16>(hrs, xsrc[j] + (((uint32_t)nx << 7) >> ((xsh >> (2 * j)) & 3u)), st + (wave * T5 + j) * 1024);
         const uint32_t wstep = (uint32_t)(nx >> 1) * (uint32_t)kCodeStep + (uint32_t)(nx & 1) * 32;
 #pragma unroll
         for (int j = 0; j < 2; ++j) lds_fill<16>(wrs, wsrc[j] + wstep, st + kDnW + (2 * wave + j) * 1024);
@@ -331,22 +437,35 @@ __device__ __forceinline__ void down_tile(int H, int I, uint32_t plane, const Gr
         __builtin_amdgcn_sched_barrier(0);
         fill(nxt, nx);
         u32x4 wc[2];
+        uint32_t ws[2], ls[T5];
         float fs[2];
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
             wc[f] = lds_ld<u32x4>(cur + wro[f]);
-            fs[f] = e8m0_to_f32(lds_ld<uint8_t>(cur + sro[f] + 2 * (sc & 1)));
+            ws[f] = lds_ld<uint8_t>(cur + sro[f] + 2 * (sc & 1));
+            fs[f] = e8m0_to_f32(ws[f]);
         }
-        constexpr int U = 4 * T5;    // units (m, b); a unit reads the hi and lo operands of column tile b
-        bf16x8 bh[U], bl[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            bh[u] = __builtin_bit_cast(bf16x8, lds_ld<u32x4>(cur + roff[u / T5] + (u % T5) * 32 * 256));
-            bl[u] = __builtin_bit_cast(bf16x8, lds_ld<u32x4>(cur + roff[4 + u / T5] + (u % T5) * 32 * 256));
-        }
+        for (int b = 0; b < T5; ++b) ls[b] = lds_ld<uint8_t>(cur + soff + b * 32 * 256);
+        // units: (m, b) = (u / T5, u % T5) for u < 4 T5, one hi read and two
+        // bf16 MFMAs each; then one per column tile b, two lo reads and two
+        // scaled MFMAs
+        constexpr int UH = 4 * T5;
+        int rxs = rx, lxs = lx;
+        asm volatile("" : "+v"(rxs), "+v"(lxs));
+        bf16x8 bh[UH];
+        u32x4 bl[T5][2];
+#pragma unroll
+        for (int u = 0; u < UH; ++u)
+            bh[u] = __builtin_bit_cast(bf16x8,
+                                       lds_ld<u32x4>(cur + rbase + 16 * ((u / T5) ^ rxs) + (u % T5) * 32 * 256));
+#pragma unroll
+        for (int b = 0; b < T5; ++b)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) bl[b][q] = lds_ld<u32x4>(cur + lbase + 32 * (q ^ lxs) + b * 32 * 256);
         bf16x8 a[2];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
+        for (int u = 0; u < UH; ++u) {
             const int m = u / T5, b = u % T5;
             if (b == 0) {
 #pragma unroll
@@ -354,10 +473,12 @@ __device__ __forceinline__ void down_tile(int H, int I, uint32_t plane, const Gr
             }
 #pragma unroll
             for (int f = 0; f < 2; ++f) acc[f][b] = mfma32x32x16(a[f], bh[u], acc[f][b]);
-#pragma unroll
-            for (int f = 0; f < 2; ++f) acc[f][b] = mfma32x32x16(a[f], bl[u], acc[f][b]);
         }
-        pipeline_order<U, T5 + 3, 4, 2, 4>();
+#pragma unroll
+        for (int b = 0; b < T5; ++b)
+#pragma unroll
+            for (int f = 0; f < 2; ++f) acc[f][b] = mfma_f4_f8(wc[f], bl[b][0], bl[b][1], ws[f], ls[b], acc[f][b]);
+        pipeline_order_down<T5>();
     });
 
     // lane (lc, h), element i: row orow0 + 64 w + 32 f + 8 (i / 4) + 4h + i % 4, token column 32 b + lc
@@ -376,8 +497,8 @@ __device__ __forceinline__ void down_tile(int H, int I, uint32_t plane, const Gr
     }
 }
 
-// hbuf: the h hi plane followed by the lo plane, `plane` = P * I elements
-// each; 2 * plane * 2 < 2^31 bytes.
+// hbuf: the h hi plane (bf16, `plane` = P * I elements), then the lo codes
+// and scale slots as the gate/up GEMM stores them; 4 * plane < 2^31 bytes.
 __global__ __launch_bounds__(kThreads) void ffn_down_gemm(int H, int I, GroupView gv,
                                                           const uint16_t *__restrict__ hbuf, uint32_t plane,
                                                           float *__restrict__ y) {
