@@ -77,8 +77,8 @@ struct WsLayout {
     size_t rank;       // int32 [P]: rank of a pair among its chunk's pairs of that expert
     size_t plist;      // int32 [P]: pair ids t*k+j grouped by expert, increasing inside
     size_t tlist;      // int32 [max_tiles]: token tiles, distinct-expert index | part << 10
-    size_t hbuf;       // uint16 [2][P][I]: SwiGLU output as a bf16 hi part and the lo remainder (bf16; on
-                       // the prefill GEMM path e4m3 codes and scale slots in the lo half)
+    size_t hbuf;       // uint16 [2][P][I]: SwiGLU output as bf16 hi and lo parts (the prefill GEMMs
+                       // keep three planes of e4m3 codes and their scale slots here instead)
     size_t ybuf;       // float [P][H]: per-pair expert outputs
     size_t total;
     int nchunks;

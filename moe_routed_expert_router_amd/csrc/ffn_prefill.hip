@@ -1,10 +1,12 @@
 // Grouped SwiGLU expert FFN, prefill path (many tokens per expert).
 //
 // With ~128 tokens per expert the FFN is a real dense contraction, so it runs
-// as a grouped GEMM on 32x32x16 bf16 MFMAs (on gfx950 the 32x32 form issues
-// twice the flops per cycle of the 16x16x32 form).  The MXFP4 weights are
-// converted in registers to exact bf16 (scaled fp4 converts), so the tokens
-// enter the MFMA unchanged.  A work tile is (expert, up to kPT = 160 of its
+// as a grouped GEMM on the matrix cores.  gate/up: 32x32x16 bf16 MFMAs (on
+// gfx950 the 32x32 form issues twice the flops per cycle of the 16x16x32
+// form), the MXFP4 weights converted in registers to exact bf16 (scaled fp4
+// converts), so the bf16 tokens enter unchanged.  down: the scaled 32x32x64
+// fp4 x fp8 MFMA on the W2 codes as stored, h entering as three MXFP8 terms
+// (2.3 times the bf16 rate per flop).  A work tile is (expert, up to kPT = 160 of its
 // tokens, a block of weight rows); the grouping lists the (expert, token
 // tile) pairs on the device.
 //
@@ -16,12 +18,11 @@
 // then reads its weight codes from LDS, converts them once per MFMA sub-step
 // and runs the MFMAs, with the token operand reads issued a few MFMAs ahead.
 // gate/up: operand 0 = 32 gate rows, operand 1 = the matching 32 up rows (a
-// block covers 256 columns of h); the epilogue stores h = silu(g) * u as a
-// bf16 hi part and the remainder lo as MXFP8 (e4m3 codes, one e8m0 scale per
-// 32 columns).  down: two 32-row operands of W2 (a block covers 512 output
-// rows); h hi enters bf16 MFMAs on the converted weights, h lo one scaled
-// fp4 x fp8 MFMA per K step on the weight codes as stored, both into the same
-// accumulators.
+// block covers 256 columns of h); the epilogue stores h = silu(g) * u as three
+// MXFP8 terms (e4m3 codes, one e8m0 scale per 32 columns each), the second
+// and third holding what the terms before leave.  down: two 32-row operands
+// of W2 (a block covers 512 output rows); per K step each h term enters one
+// scaled fp4 x fp8 MFMA that takes the W2 codes and scales as stored.
 //
 // K permutation: inside one K step, lane half h (lanes 32h..32h+31) covers a
 // contiguous run of K made of whole MX blocks, and MFMA sub-step m takes the
@@ -86,7 +87,15 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)v, true);
 }
 
+// silu(g) = g / (1 + e^-g) with the reciprocal instruction (about 1 ulp) in
+// place of an IEEE division (a ten-instruction sequence): the epilogue runs
+// it on every h element of a tile.  g << 0 gives -0, as the division does.
+__device__ __forceinline__ float silu_rcp(float g) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
+
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // D += W x H over one 64-K step on the scaled 32x32x64 MFMA: A = 32 weight
 // rows as fp4 codes (lane half h: K [32h, 32h+32), element order) with their
@@ -142,31 +151,6 @@ __device__ __forceinline__ void pipeline_order() {
         __builtin_amdgcn_sched_group_barrier(0x008, MPU, 0);                       // MFMA
         if (u + kAhead < U) __builtin_amdgcn_sched_group_barrier(0x100, RPU, 0);   // DS read
     }
-    __builtin_amdgcn_sched_barrier(0);
-}
-
-// The down step's order: its T5 + 3 fills, the weight and scale reads
-// (4 + T5) and the operand reads of the first kAhead units, then per unit its
-// two MFMAs and the reads of the unit kAhead later (one for a hi unit, two
-// for a lo unit; the 4 T5 hi units come first).
-template <int T5>
-__device__ __forceinline__ void pipeline_order_down() {
-    static_assert(kAhead == 2 && 4 * T5 > kAhead, "unit counts below assume two units ahead");
-    constexpr int UH = 4 * T5, U = UH + T5;
-    __builtin_amdgcn_sched_group_barrier(0x020, T5 + 3, 0);          // VMEM (LDS fills)
-    __builtin_amdgcn_sched_group_barrier(0x100, 4 + T5 + kAhead, 0); // DS reads
-#pragma unroll
-    for (int u = 0; u < UH - kAhead; ++u) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-#pragma unroll
-    for (int u = UH - kAhead; u < U - kAhead; ++u) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-#pragma unroll
-    for (int u = U - kAhead; u < U; ++u) __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -283,42 +267,59 @@ __device__ __forceinline__ void gate_up_tile(__amdgpu_buffer_rsrc_t xrs, int H, 
 
     // lane (lc, h), element i: h column hcol + 8 (i / 4) + 4h + i % 4, token
     // column 32 b + lc.  The wave's 32 columns are one MX block of h along I,
-    // half in each lane half.  h = hi + lo: hi is h rounded to bf16, lo = h -
-    // hi (exact in fp32) is stored as e4m3 codes under one e8m0 scale per
-    // (token, block), the least power of two that puts the block's largest
-    // |lo| at or below 448.  Lo plane (bytes from hlo): codes [P][I], then
-    // scale slots [P][I/64][16] (bytes 0 and 1 of a slot: the two blocks of
-    // a 64-column step).
+    // half in each lane half.  h ~ q0 2^e0 + q1 2^e1 + q2 2^e2: term t holds
+    // the e4m3 codes of the remainder r_t (r_0 = h, r_t+1 = r_t - q_t 2^e_t,
+    // exact in fp32) under the e8m0 scale e_t.  e0 is the least power of two
+    // that puts the block's largest |h| at or below 448; a remainder is at
+    // most half an e4m3 step of the term before (16 at the top, [256, 448)
+    // binade), so e_t = e0 - 4t keeps term 1's codes at or below 256 and term
+    // 2's at or below 128 (no code saturates; clamped at e8m0's -127, the
+    // codes only shrink).  hbuf bytes: term t's codes [P][I] from t * plane, then
+    // scale slots [P][I/64][16] from 3 plane; byte 4 b2 + t of a slot is term
+    // t's scale for block b2 (0, 1) of the 64-column step.
     const size_t hcol = (size_t)t.rb * 256 + 32 * wave;
     const size_t plane = (size_t)(hlo - hhi);
-    uint8_t *lq = reinterpret_cast<uint8_t *>(hlo);
-    uint8_t *ls = lq + plane;
+    uint8_t *hq = reinterpret_cast<uint8_t *>(hhi);
+    uint8_t *hs = hq + 3 * plane;
 #pragma unroll
     for (int b = 0; b < T5; ++b) {
         const int c = 32 * b + lc;
-        uint32_t hi[16];
-        float r[16], amax = 0.f;
+        float r[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float v = silu(acc[0][b][i]) * acc[1][b][i];
-            hi[i] = f32_to_bf16_bits(v);
-            r[i] = v - __uint_as_float(hi[i] << 16);
-            amax = fmaxf(amax, fabsf(r[i]));
-        }
+        for (int i = 0; i < 16; ++i) r[i] = silu_rcp(acc[0][b][i]) * acc[1][b][i];
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(r[i]));
         amax = fmaxf(amax, __shfl_xor(amax, 32));   // the block's other 16 columns
-        const int e = e8m0_for(amax);
-        const float inv = ldexpf(1.f, -e);
+        const int e0 = e8m0_for(amax);
+        uint32_t q[3][4], sc = 0;
+#pragma unroll
+        for (int tm = 0; tm < 3; ++tm) {
+            const int e = e0 - 4 * tm < -127 ? -127 : e0 - 4 * tm;
+            const float inv = ldexpf(1.f, -e), sv = ldexpf(1.f, e);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                q[tm][j] = e4m3x4(r[4 * j] * inv, r[4 * j + 1] * inv, r[4 * j + 2] * inv, r[4 * j + 3] * inv);
+                if (tm < 2) {   // codes times 2^e, two per convert (low, high half)
+                    const f32x2 d0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(q[tm][j], sv, false);
+                    const f32x2 d1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(q[tm][j], sv, true);
+                    r[4 * j] -= d0[0];
+                    r[4 * j + 1] -= d0[1];
+                    r[4 * j + 2] -= d1[0];
+                    r[4 * j + 3] -= d1[1];
+                }
+            }
+            sc |= (uint32_t)(e + 127) << (8 * tm);
+        }
         if (c < t.nt) {
             const size_t row = (size_t)(t.q0 + c);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const size_t off = row * I + hcol + 8 * j + 4 * h;
-                *reinterpret_cast<uint2 *>(hhi + off) =
-                    make_uint2(hi[4 * j] | (hi[4 * j + 1] << 16), hi[4 * j + 2] | (hi[4 * j + 3] << 16));
-                *reinterpret_cast<uint32_t *>(lq + off) =
-                    e4m3x4(r[4 * j] * inv, r[4 * j + 1] * inv, r[4 * j + 2] * inv, r[4 * j + 3] * inv);
-            }
-            if (h == 0) ls[(row * (I / 64) + hcol / 64) * 16 + (wave & 1)] = (uint8_t)(e + 127);
+            for (int tm = 0; tm < 3; ++tm)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<uint32_t *>(hq + tm * plane + row * I + hcol + 8 * j + 4 * h) = q[tm][j];
+            if (h == 0)
+                *reinterpret_cast<uint32_t *>(hs + (row * (I / 64) + hcol / 64) * 16 + 4 * (wave & 1)) = sc;
         }
     }
 }
@@ -343,13 +344,11 @@ __global__ __launch_bounds__(kThreads) void ffn_gate_up_gemm(const uint16_t *__r
 
 // ---------------------------------------------------------------------------
 // down: K step 64.  Lane half h holds K [32h, 32h+32) of the step (MX block
-// h) of its W2 row; h hi enters four bf16 MFMAs (sub-step m = 0..3 takes
-// elements 8m..8m+7, the token operand read with the same permutation) and h
-// lo one scaled fp4 x fp8 MFMA on the same W2 codes, as stored, with their
-// scale bytes.
-// Stage: h tile (a row holds, for the step's 64 K, h hi in chunks 0..7, the
-// e4m3 codes of h lo in chunks 8..11 and its scale slot in chunk 12; chunks
-// 13..15 are not filled) | W2 codes [512 rows][32 B] | scales [512 rows][4 B]
+// h) of its W2 row as stored (16 code bytes, one scale byte); each of h's
+// three e4m3 terms enters one scaled fp4 x fp8 MFMA per column tile.
+// Stage: h tile (a row holds, for the step's 64 K, term t's codes in chunks
+// 4t..4t+3 and the scale slot in chunk 12; chunks 13..15 are not filled) |
+// W2 codes [512 rows][32 B] | scales [512 rows][4 B]
 // (the aligned dword holding the step's two scale bytes and those of its pair
 // step); weight row r = 64 w + 32 f + c holds its 2 chunks in slots
 // k ^ ((r >> 3) & 1).
@@ -367,30 +366,24 @@ __device__ __forceinline__ void down_tile(int H, int I, uint32_t plane, const Gr
     const BlobLayout L = BlobLayout::make(H, I);
     const __amdgpu_buffer_rsrc_t wrs = buffer_rsrc(t.base, (uint32_t)L.bytes);
     const uint32_t orow0 = (uint32_t)t.rb * 512;
-    // h rows 4 (w T5 + j) .. +3.  hbuf bytes: hi [P][I] bf16 from 0, lo codes
-    // [P][I] from 2 plane, lo scale slots [P][I/64][16] from 3 plane.  A
-    // fill's step offset is nx * 128 >> shift: shift 0 for hi, 1 for lo codes,
-    // 3 for the scale slot; xsh holds 2 bits per fill.  Chunks 13..15 take an
-    // offset past the buffer's end (kNoFill + at most 16 I / 64 < 2^32), where
-    // a buffer load reads nothing and returns zeros: no branch in the K loop.
+    // h rows 4 (w T5 + j) .. +3.  hbuf bytes: term t's codes [P][I] from t *
+    // plane, scale slots [P][I/64][16] from 3 plane.  A fill's step offset is
+    // 64 nx for the codes, 16 nx for the scale slot (xsl: one bit per fill).
+    // Chunks 13..15 take an offset past the buffer's end (kNoFill + at most
+    // 16 I / 64 < 2^32), where a buffer load reads nothing and returns zeros:
+    // no branch in the K loop.
     constexpr uint32_t kNoFill = 0x80000000u;
-    uint32_t xsrc[T5], xsh = 0;
+    uint32_t xsrc[T5], xsl = 0;
 #pragma unroll
     for (int j = 0; j < T5; ++j) {
         const int c = 4 * (wave * T5 + j) + (lane >> 4), chunk = (lane & 15) ^ (c & 15);
         const uint32_t row = (uint32_t)(t.q0 + (c < t.nt ? c : 0));
-        uint32_t sh;
-        if (chunk < 8) {
-            xsrc[j] = (row * (uint32_t)I + chunk * 8) * 2;
-            sh = 0;
-        } else if (chunk < 12) {
-            xsrc[j] = 2 * plane + row * (uint32_t)I + (chunk - 8) * 16;
-            sh = 1;
+        if (chunk < 12) {
+            xsrc[j] = (uint32_t)(chunk >> 2) * plane + row * (uint32_t)I + (chunk & 3) * 16;
         } else {
             xsrc[j] = chunk == 12 ? 3 * plane + row * (uint32_t)(I / 4) : kNoFill;
-            sh = 3;
+            xsl |= 1u << j;
         }
-        xsh |= sh << (2 * j);
     }
     uint32_t wsrc[2];
     const size_t nst = I / 128;   // tiled blob: a 64-K step is one half of each row's 64 bytes of a tile
@@ -407,19 +400,18 @@ __device__ __forceinline__ void down_tile(int H, int I, uint32_t plane, const Gr
         wro[f] = kDnW + r * 32 + 16 * (h ^ ((r >> 3) & 1));
         sro[f] = kDnS + 4 * r + h;   // + 2 for odd steps
     }
-    // token row lc (column tile b adds 32 rows): hi chunk 4h + m in slot
-    // (4h ^ (lc & 12)) + (m ^ (lc & 3)); lo chunk 8 + 2q + h in slot
-    // ((8 + h) ^ (lc & 13)) + 2 (q ^ ((lc >> 1) & 1)); scale byte h of chunk
-    // 12.  Two registers each give the hi and lo offsets (made opaque per
-    // step, so the six offsets are not hoisted into registers).
-    const int rbase = lc * 256 + 16 * ((4 * h) ^ (lc & 12)), rx = lc & 3;
-    const int lbase = lc * 256 + 16 * ((8 + h) ^ (lc & 13)), lx = (lc >> 1) & 1;
-    const int soff = lc * 256 + 16 * (12 ^ (lc & 15)) + h;
+    // token row lc (column tile b adds 32 rows): term t's bytes [16h, 16h+16)
+    // and [32+16h, 32+16h+16) of the step are chunks 4t + 2q + h (q = 0, 1),
+    // in slot ((4t + 2q) ^ (lc & 14)) + (h ^ (lc & 1)); the three scale bytes
+    // of block h are the dword at byte 4h of chunk 12.  Two registers give
+    // the six offsets (made opaque per step, so they are not hoisted).
+    const int xbase = lc * 256 + 16 * (h ^ (lc & 1)), xx = lc & 14;
+    const int soff = lc * 256 + 16 * (12 ^ (lc & 15)) + 4 * h;
 
     auto fill = [&](uint8_t *st, int nx) {
 #pragma unroll
         for (int j = 0; j < T5; ++j)
-            lds_fill<16>(hrs, xsrc[j] + (((uint32_t)nx << 7) >> ((xsh >> (2 * j)) & 3u)), st + (wave * T5 + j) * 1024);
+            lds_fill<16>(hrs, xsrc[j] + ((uint32_t)nx << (((xsl >> j) & 1u) ? 4 : 6)), st + (wave * T5 + j) * 1024);
         const uint32_t wstep = (uint32_t)(nx >> 1) * (uint32_t)kCodeStep + (uint32_t)(nx & 1) * 32;
 #pragma unroll
         for (int j = 0; j < 2; ++j) lds_fill<16>(wrs, wsrc[j] + wstep, st + kDnW + (2 * wave + j) * 1024);
@@ -437,48 +429,32 @@ __device__ __forceinline__ void down_tile(int H, int I, uint32_t plane, const Gr
         __builtin_amdgcn_sched_barrier(0);
         fill(nxt, nx);
         u32x4 wc[2];
-        uint32_t ws[2], ls[T5];
-        float fs[2];
+        uint32_t ws[2], xs[T5];
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
             wc[f] = lds_ld<u32x4>(cur + wro[f]);
             ws[f] = lds_ld<uint8_t>(cur + sro[f] + 2 * (sc & 1));
-            fs[f] = e8m0_to_f32(ws[f]);
         }
 #pragma unroll
-        for (int b = 0; b < T5; ++b) ls[b] = lds_ld<uint8_t>(cur + soff + b * 32 * 256);
-        // units: (m, b) = (u / T5, u % T5) for u < 4 T5, one hi read and two
-        // bf16 MFMAs each; then one per column tile b, two lo reads and two
-        // scaled MFMAs
-        constexpr int UH = 4 * T5;
-        int rxs = rx, lxs = lx;
-        asm volatile("" : "+v"(rxs), "+v"(lxs));
-        bf16x8 bh[UH];
-        u32x4 bl[T5][2];
+        for (int b = 0; b < T5; ++b) xs[b] = lds_ld<uint32_t>(cur + soff + b * 32 * 256);
+        // units (t, b) = (u / T5, u % T5): two reads of term t, two MFMAs
+        constexpr int U = 3 * T5;
+        int xxs = xx;
+        asm volatile("" : "+v"(xxs));
+        u32x4 bx[U][2];
 #pragma unroll
-        for (int u = 0; u < UH; ++u)
-            bh[u] = __builtin_bit_cast(bf16x8,
-                                       lds_ld<u32x4>(cur + rbase + 16 * ((u / T5) ^ rxs) + (u % T5) * 32 * 256));
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int b = 0; b < T5; ++b)
+            for (int q = 0; q < 2; ++q)
+                bx[u][q] = lds_ld<u32x4>(cur + xbase + 16 * ((4 * (u / T5) + 2 * q) ^ xxs) + (u % T5) * 32 * 256);
 #pragma unroll
-            for (int q = 0; q < 2; ++q) bl[b][q] = lds_ld<u32x4>(cur + lbase + 32 * (q ^ lxs) + b * 32 * 256);
-        bf16x8 a[2];
+        for (int u = 0; u < U; ++u) {
+            const int tm = u / T5, b = u % T5;
+            const uint32_t s = (xs[b] >> (8 * tm)) & 0xffu;
 #pragma unroll
-        for (int u = 0; u < UH; ++u) {
-            const int m = u / T5, b = u % T5;
-            if (b == 0) {
-#pragma unroll
-                for (int f = 0; f < 2; ++f) a[f] = fp4x8_to_bf16x8(wc[f][m], fs[f]);
-            }
-#pragma unroll
-            for (int f = 0; f < 2; ++f) acc[f][b] = mfma32x32x16(a[f], bh[u], acc[f][b]);
+            for (int f = 0; f < 2; ++f) acc[f][b] = mfma_f4_f8(wc[f], bx[u][0], bx[u][1], ws[f], s, acc[f][b]);
         }
-#pragma unroll
-        for (int b = 0; b < T5; ++b)
-#pragma unroll
-            for (int f = 0; f < 2; ++f) acc[f][b] = mfma_f4_f8(wc[f], bl[b][0], bl[b][1], ws[f], ls[b], acc[f][b]);
-        pipeline_order_down<T5>();
+        pipeline_order<U, T5 + 3, 4 + T5, 2, 2>();
     });
 
     // lane (lc, h), element i: row orow0 + 64 w + 32 f + 8 (i / 4) + 4h + i % 4, token column 32 b + lc
@@ -497,8 +473,8 @@ __device__ __forceinline__ void down_tile(int H, int I, uint32_t plane, const Gr
     }
 }
 
-// hbuf: the h hi plane (bf16, `plane` = P * I elements), then the lo codes
-// and scale slots as the gate/up GEMM stores them; 4 * plane < 2^31 bytes.
+// hbuf: h as the gate/up GEMM stores it (three planes of P * I = `plane`
+// e4m3 codes, then the scale slots); 4 * plane < 2^31 bytes.
 __global__ __launch_bounds__(kThreads) void ffn_down_gemm(int H, int I, GroupView gv,
                                                           const uint16_t *__restrict__ hbuf, uint32_t plane,
                                                           float *__restrict__ y) {

@@ -4,10 +4,9 @@ Bars (stated for the layer): expert indices and gathered bytes bit-exact;
 layer outputs within max|gpu - oracle| <= 2e-2 * RMS(oracle).  The tests also
 hold the path to the tighter bound its arithmetic gives (TIGHT): weights and
 activations enter the matrix cores exactly, h carries ~16 bits on the decode
-kernels (bf16 hi + lo) and ~12 on the prefill GEMMs (bf16 hi + an e4m3 lo
-under one e8m0 scale per 32 columns; measured 3-4e-4 of RMS there), sums are
-fp32 — so a dropped block scale or a mis-indexed row, which could hide under
-2e-2, fails here.
+kernels (bf16 hi + lo) and three e4m3 terms under e8m0 block scales on the
+prefill GEMMs (measured ~2e-4 of RMS there), sums are fp32 — so a dropped
+block scale or a mis-indexed row, which could hide under 2e-2, fails here.
 
 Index rules, since fp32 (GPU) and fp64 (oracle) logits differ in rounding:
   R1  the oracle's selection applied to the GPU's own fp32 logits equals the
