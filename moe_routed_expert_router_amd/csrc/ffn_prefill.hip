@@ -175,7 +175,10 @@ template <int T5>
 __device__ __forceinline__ void gate_up_tile(__amdgpu_buffer_rsrc_t xrs, int H, int I, int k, const GroupView &gv,
                                              const Tile &t, uint8_t *sa, uint8_t *sb, uint16_t *__restrict__ hhi,
                                              uint16_t *__restrict__ hlo) {
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lc = lane & 31, h = lane >> 5;
+    // the wave index as a scalar, so the fills' LDS destinations stay in
+    // scalar registers
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lc = lane & 31,
+              h = lane >> 5;
     const BlobLayout L = BlobLayout::make(H, I);
     const __amdgpu_buffer_rsrc_t wrs = buffer_rsrc(t.base, (uint32_t)L.bytes);
     // fills of this wave (byte offsets; the step adds its K offset)
@@ -362,7 +365,10 @@ template <int T5>
 __device__ __forceinline__ void down_tile(int H, int I, uint32_t plane, const GroupView &gv, const Tile &t,
                                           uint8_t *sa, uint8_t *sb, __amdgpu_buffer_rsrc_t hrs,
                                           float *__restrict__ y) {
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lc = lane & 31, h = lane >> 5;
+    // the wave index as a scalar, so the fills' LDS destinations stay in
+    // scalar registers
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lc = lane & 31,
+              h = lane >> 5;
     const BlobLayout L = BlobLayout::make(H, I);
     const __amdgpu_buffer_rsrc_t wrs = buffer_rsrc(t.base, (uint32_t)L.bytes);
     const uint32_t orow0 = (uint32_t)t.rb * 512;
