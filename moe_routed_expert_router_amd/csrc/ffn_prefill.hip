@@ -6,17 +6,18 @@
 // form), the MXFP4 weights converted in registers to exact bf16 (scaled fp4
 // converts), so the bf16 tokens enter unchanged.  down: the scaled 32x32x64
 // fp4 x fp8 MFMA on the W2 codes as stored, h entering as three MXFP8 terms
-// (2.3 times the bf16 rate per flop).  A work tile is (expert, up to kPT = 160 of its
-// tokens, a block of weight rows); the grouping lists the (expert, token
-// tile) pairs on the device.
+// (2.3 times the bf16 rate per flop).  A work tile is (expert, up to kPT =
+// 160 of its tokens, a block of weight rows); the grouping lists the
+// (expert, token tile) pairs on the device.
 //
 // A block has 8 waves, each owning two 32-row weight operands and all of the
 // tile's (up to five) 32-token column tiles.  Every K step, the block copies
-// the next step's token (h) tile, weight codes and scales from global memory
-// straight into LDS (buffer loads with an LDS destination, double-buffered);
-// the global traffic per step is the block's unique bytes, once.  Each wave
-// then reads its weight codes from LDS, converts them once per MFMA sub-step
-// and runs the MFMAs, with the token operand reads issued a few MFMAs ahead.
+// the next step's token (x or h) tile, weight codes and scales from global
+// memory straight into LDS (buffer loads with an LDS destination,
+// double-buffered); the global traffic per step is the block's unique bytes,
+// once.  Each wave then reads its weight codes from LDS (the gate/up converts
+// them once per MFMA sub-step) and runs the MFMAs, with the token operand
+// reads issued a few MFMAs ahead.
 // gate/up: operand 0 = 32 gate rows, operand 1 = the matching 32 up rows (a
 // block covers 256 columns of h); the epilogue stores h = silu(g) * u as three
 // MXFP8 terms (e4m3 codes, one e8m0 scale per 32 columns each), the second
@@ -24,10 +25,11 @@
 // of W2 (a block covers 512 output rows); per K step each h term enters one
 // scaled fp4 x fp8 MFMA that takes the W2 codes and scales as stored.
 //
-// K permutation: inside one K step, lane half h (lanes 32h..32h+31) covers a
-// contiguous run of K made of whole MX blocks, and MFMA sub-step m takes the
-// m-th 8 elements of that run.  The token operand is read with the same
-// permutation, so each MFMA is an exact partial dot product.
+// K permutation (gate/up): inside one K step, lane half h (lanes
+// 32h..32h+31) covers a contiguous run of K made of whole MX blocks, and MFMA
+// sub-step m takes the m-th 8 elements of that run.  The token operand is
+// read with the same permutation, so each MFMA is an exact partial dot
+// product.  (The down GEMM's scaled MFMA takes K in its own operand order.)
 //
 // Blocks are numbered so that all row blocks of one token tile land on the
 // same XCD (consecutive blocks go to consecutive XCDs) and share the tile's
