@@ -12,8 +12,9 @@ if not torch.cuda.is_available():
 
 import moe_routed_expert_router_amd as moe  # noqa: E402
 from oracle import gather as ogather  # noqa: E402
+from oracle import route as oroute  # noqa: E402
 from synth import gen  # noqa: E402
-from tests.gpu_checks import check_out, check_route, oracle_out, route_on_gpu  # noqa: E402
+from tests.gpu_checks import TIGHT, check_out, check_route, oracle_out, route_on_gpu  # noqa: E402
 from tests.gpu_setup import Layer, Stack  # noqa: E402
 
 
@@ -222,6 +223,32 @@ def test_gemm_tile_shapes(E, k, T):
     ref = oracle_out(L)
     assert np.array_equal(ids, ref["ids"])
     check_out(out.cpu().numpy(), ref["out"])
+
+
+def test_gemm_rows_over_six_decades():
+    """Grouped-GEMM path with each token scaled by 10^u, u uniform in [-3, 3]:
+    every output row stays within the tight bound of its own RMS, so the
+    GEMMs keep a relative precision per token whatever its magnitude (h's
+    e4m3 terms take their scales per 32 columns of a token; silu of a large
+    negative gate underflows to -0 on both sides).  The routing margins of
+    these seeded tokens are at least 9e-5 of their largest logit, far above
+    fp32 rounding, so the ids must match exactly."""
+    wl = gen.Workload("gemm_range", 512, 256, 16, 2, 700, seed=7)
+    x = oroute.bf16_bits_to_f32(gen.tokens_bf16(wl.seed, 0, wl.tokens, wl.hidden)).astype(np.float32)
+    s = (10.0 ** np.random.default_rng(3).uniform(-3, 3, size=(wl.tokens, 1))).astype(np.float32)
+    L = Layer(wl, x_np=gen.bf16_round_bits(x * s))
+    try:
+        out = L.forward().cpu().numpy()
+        ref = oracle_out(L)
+        assert np.array_equal(L.ids.cpu().numpy(), ref["ids"])
+        got, want = out.astype(np.float64), ref["out"].astype(np.float64)
+        row_rms = np.sqrt(np.mean(want * want, axis=1))
+        err = np.max(np.abs(got - want), axis=1) / row_rms
+        print(f"rows over six decades: row RMS {row_rms.min():.2e}..{row_rms.max():.2e}, "
+              f"max row err / row RMS = {err.max():.2e}")
+        assert err.max() <= TIGHT, err.max()
+    finally:
+        L.close()
 
 
 def test_wave_path_for_unaligned_hidden():
