@@ -99,9 +99,9 @@ __device__ __forceinline__ void split3(const float *v, bf16x8 &hi, bf16x8 &mid, 
 // BT tokens (128, or 64 for at most kRgSmallT tokens, giving more blocks) x
 // 64 experts.  Per K step of 32 it copies the token rows and the fp32 router
 // rows straight into LDS (a ring of four stages, three steps ahead: one
-// step's compute is far shorter than an L2 round trip), splits the router
-// rows once for the whole block into three bf16 planes (native bf16
-// converts), then each wave runs a 32-expert x BT/2-token tile from LDS.
+// step's compute is far shorter than an L2 round trip), then each wave runs a
+// 32-expert x BT/2-token tile from LDS, splitting its router values into the
+// three bf16 terms in registers as it reads them (native bf16 converts).
 // Every block of a token tile sits on the same XCD (consecutive blocks go to
 // consecutive XCDs), so the tile's token rows come into that XCD's L2 once
 // for all the expert tiles.  (A wave that reads its operands from global
@@ -110,12 +110,15 @@ __device__ __forceinline__ void split3(const float *v, bf16x8 &hi, bf16x8 &mid, 
 // traffic and VALU work that this layout removes.)
 constexpr int kRgE = 64, kRgK = 32;               // experts per block, K step
 constexpr int kRgW = kRgE * kRgK * 4;             // fp32 router rows per stage: 128 B each
-constexpr int kRgPlane = kRgE * kRgK * 2;         // one bf16 plane of the split rows: 64 B each
 constexpr int kRgSmallT = 4096;                   // up to this many tokens, 64-token blocks (more of them)
 
-// LDS rows of 64 bytes hold their four 16-byte chunks swizzled: chunk k of
-// row c sits in slot k ^ (c & 3).
+// LDS rows of 64 bytes (token rows) hold their four 16-byte chunks swizzled:
+// chunk k of row c sits in slot k ^ (c & 3).
 __device__ __forceinline__ int rg_slot(int c, int k) { return c * 64 + 16 * (k ^ (c & 3)); }
+// Router rows of 128 bytes: chunk k of row e sits in slot k ^ ((e >> 1) & 7),
+// so 16 lanes reading one chunk of 16 consecutive rows hit 16 distinct bank
+// groups (row e's slots start at bank 32 (e & 1)).
+__device__ __forceinline__ int rg_wslot(int e, int k) { return e * 128 + 16 * (k ^ ((e >> 1) & 7)); }
 
 // grid 8 * expert tiles * ceil(token tiles / 8); 256 threads.  H % 32 == 0,
 // T * H * 2 and E * H * 4 below 2^32 (32-bit fill offsets).
@@ -132,7 +135,6 @@ __global__ __launch_bounds__(256) void route_logits_gemm(const uint16_t *__restr
     __shared__ __align__(16) uint8_t st1[kRgStage];
     __shared__ __align__(16) uint8_t st2[kRgStage];
     __shared__ __align__(16) uint8_t st3[kRgStage];
-    __shared__ __align__(16) uint8_t sp[3 * kRgPlane];
     const int net = (E + kRgE - 1) / kRgE, ntt = (T + BT - 1) / BT;
     const int b = blockIdx.x, xcd = b & 7, rest = b >> 3;
     const int et = rest % net, tt = (rest / net) * 8 + xcd;
@@ -155,10 +157,10 @@ __global__ __launch_bounds__(256) void route_logits_gemm(const uint16_t *__restr
         xsrc[j] = ((uint32_t)t * (uint32_t)H + 8 * k) * 2;
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < 2; ++j) {   // lane: row er, slot lane & 7, which holds chunk (lane & 7) ^ ((er >> 1) & 7)
         const int f = 2 * wave + j;
         const int er = 8 * f + (lane >> 3), e = ex0 + er < E ? ex0 + er : E - 1;
-        wsrc[j] = ((uint32_t)e * (uint32_t)H + 4 * (lane & 7)) * 4;
+        wsrc[j] = ((uint32_t)e * (uint32_t)H + 4 * ((lane & 7) ^ ((er >> 1) & 7))) * 4;
     }
     auto fill = [&](uint8_t *st, int k0) {
 #pragma unroll
@@ -167,16 +169,17 @@ __global__ __launch_bounds__(256) void route_logits_gemm(const uint16_t *__restr
         for (int j = 0; j < 2; ++j) lds_fill<16>(wrs, wsrc[j] + k0 * 4, st + kRgX + (2 * wave + j) * 1024);
     };
 
-    // split: thread tid converts router row tid >> 2, elements 8 (tid & 3) .. +7
-    const int se = tid >> 2, sk = tid & 3;
     // operand reads of this wave: experts 32 (wave & 1) + lc, tokens
-    // (BT / 2) (wave >> 1) + 32 b + lc for its NB column tiles b
+    // (BT / 2) (wave >> 1) + 32 b + lc for its NB column tiles b; MFMA q
+    // takes K [16q, 16q+16) of the step, lane half h its elements 8h..8h+7
+    // (router: the fp32 chunks 2 (2q + h) and 2 (2q + h) + 1)
     constexpr int NB = BT / 64;
     const int ea = 32 * (wave & 1) + lc, tb0 = (BT / 2) * (wave >> 1) + lc;
-    int aoff[2], boff[NB][2];
+    int aoff[2][2], boff[NB][2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-        aoff[q] = rg_slot(ea, 2 * q + h);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) aoff[q][p] = kRgX + rg_wslot(ea, 2 * (2 * q + h) + p);
 #pragma unroll
         for (int bb = 0; bb < NB; ++bb) boff[bb][q] = rg_slot(tb0 + 32 * bb, 2 * q + h);
     }
@@ -203,23 +206,15 @@ __global__ __launch_bounds__(256) void route_logits_gemm(const uint16_t *__restr
         // every wave is done with step s - 1, whose stage `nxt` is
         fill_barrier<2 * (XF + 2)>();
         fill(nxt, (s + 3 < S ? s + 3 : S - 1) * kRgK);
-        {
-            const float4 *src = reinterpret_cast<const float4 *>(cur + kRgX + se * 128 + 32 * sk);
-            const float4 v0 = src[0], v1 = src[1];
-            const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-            bf16x8 hi, mid, lo;
-            split3(v, hi, mid, lo);
-            const int o = rg_slot(se, sk);
-            *reinterpret_cast<bf16x8 *>(sp + o) = hi;
-            *reinterpret_cast<bf16x8 *>(sp + kRgPlane + o) = mid;
-            *reinterpret_cast<bf16x8 *>(sp + 2 * kRgPlane + o) = lo;
-        }
-        lds_barrier();
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             bf16x8 a[3], bt[NB];
-#pragma unroll
-            for (int pl = 0; pl < 3; ++pl) a[pl] = *reinterpret_cast<const bf16x8 *>(sp + pl * kRgPlane + aoff[q]);
+            {
+                const float4 v0 = *reinterpret_cast<const float4 *>(cur + aoff[q][0]);
+                const float4 v1 = *reinterpret_cast<const float4 *>(cur + aoff[q][1]);
+                const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+                split3(v, a[0], a[1], a[2]);
+            }
 #pragma unroll
             for (int bb = 0; bb < NB; ++bb) bt[bb] = *reinterpret_cast<const bf16x8 *>(cur + boff[bb][q]);
 #pragma unroll
