@@ -251,6 +251,29 @@ def test_gemm_rows_over_six_decades():
         L.close()
 
 
+def test_gemm_max_experts_and_k():
+    """Grouped-GEMM path at the ABI's largest expert count and top-k (E =
+    1024, k = 32; 300 tokens, H = 512): every expert is picked, with at most
+    21 pairs, so the tile list holds 1024 one-column-tile tiles (distinct
+    index up to 1023 in its 10-bit field); the router GEMM runs 16 expert
+    tiles and the top-k its widest form.  Routing by R1-R3, outputs within the
+    bars (the smallest oracle margin, 4.9e-5, is far above the fp32 logit
+    error at this size, so the ids must match exactly)."""
+    wl = gen.Workload("gemm_maxek", 512, 256, 1024, 32, 300, seed=11)
+    L = Layer(wl)
+    try:
+        ids_g, w_g, z_g = route_on_gpu(L)
+        check_route(L, ids_g, w_g, z_g)
+        out = L.forward()
+        torch.cuda.synchronize()
+        ref = oracle_out(L)
+        assert np.array_equal(L.ids.cpu().numpy(), ref["ids"])
+        assert len(np.unique(ref["ids"])) == 1024
+        check_out(out.cpu().numpy(), ref["out"])
+    finally:
+        L.close()
+
+
 def test_wave_path_for_unaligned_hidden():
     """T > 32 with H not a multiple of 256 runs the one-wave kernels."""
     wl = gen.Workload("h384", 384, 256, 16, 4, 48, seed=3)
