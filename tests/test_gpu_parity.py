@@ -445,6 +445,41 @@ def test_unusable_residency_entry_contributes_zero(T):
     check_out(out.cpu().numpy(), combine(w_g, y))
 
 
+@pytest.mark.parametrize("mode", ["invalid_ids", "unusable_entry"])
+def test_gemm_invalid_ids_and_unusable_entry(mode):
+    """The grouped-GEMM path (100 tokens, H = 512): picks with an id outside
+    [0, E) are left out of the grouping and of the combine; an expert whose
+    residency entry is outside [0, n_hot) makes its pairs contribute zero (its
+    gate/up tiles skip it, its down tiles write zeros).  Either way the
+    output is the oracle's combine with those pairs' outputs set to zero."""
+    wl = gen.Workload("gemm_bad", 512, 256, 16, 3, 100, seed=5)
+    L = Layer(wl)
+    try:
+        ids_g, w_g, _ = route_on_gpu(L)
+        ref = oracle_out(L)
+        assert np.array_equal(ids_g, ref["ids"])
+        y = ref["y"].copy()
+        ids_in, r = ids_g.copy(), L.residency
+        if mode == "invalid_ids":
+            for t, j, v in ((0, 1, -1), (17, 0, L.E), (63, 2, -5), (99, 1, L.E + 3)):
+                ids_in[t, j] = v
+                y[t, j] = 0
+        else:
+            e_bad = int(ids_g[40, 0])
+            slot = L.slot_np.copy()
+            slot[e_bad] = L.n_hot + 7
+            r = moe.residency(torch.from_numpy(slot).cuda(), L.hot_base, None, None, L.n_hot, 0)
+            y[ids_g == e_bad] = 0
+        out = torch.empty((L.T, L.H), dtype=torch.float32, device="cuda")
+        moe.moe_expert_ffn(L.shape, L.x, torch.from_numpy(ids_in).cuda(), torch.from_numpy(w_g).cuda(), r, out,
+                           L.ws)
+        torch.cuda.synchronize()
+        from oracle.ffn import combine
+        check_out(out.cpu().numpy(), combine(w_g, y))
+    finally:
+        L.close()
+
+
 def test_zero_tokens_is_a_no_op():
     L = Layer(gen.workload("tiny"), T=4)
     L.out.fill_(7.0)
