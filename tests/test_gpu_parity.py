@@ -509,11 +509,13 @@ def test_gpu_error_paths():
 
 
 @pytest.mark.parametrize("name,T,delta", [("tiny", 8, 0.0), ("hotcold8", 8, 0.0), ("hotcold8", 32, 3.0),
-                                          ("hotcold8", 1, 3.0), ("hotcold8", 1, 0.0), ("hotcold8", 4, 3.0)])
+                                          ("hotcold8", 1, 3.0), ("hotcold8", 1, 0.0), ("hotcold8", 4, 3.0),
+                                          ("hotcold8", 40, 3.0), ("hotcold8", 300, 0.0)])
 def test_graph_replay_matches_eager(name, T, delta):
     """The layer captured in a HIP graph gives the eager result on every
     replay, with eager work and synchronisations between replays (with cold
-    picks the capture holds the side-stream fork and join)."""
+    picks the capture holds the side-stream fork and join; from 33 tokens the
+    grouping kernels and the grouped GEMMs are captured)."""
     L = Layer(gen.workload(name), T=T)
     try:
         if delta:
