@@ -203,8 +203,10 @@ def ffn_bytes(w: Workload, picks_per_step: list[np.ndarray]) -> dict:
 
 
 def layer_bytes(layer_picks) -> dict:
-    """As ffn_bytes, over (layer, ids of one launch) pairs (layers may differ)."""
-    gu, dn, cold_bytes, uniq = [], [], [], []
+    """As ffn_bytes, over (layer, ids of one launch) pairs (layers may differ).
+    "combine": the separate combine kernel's y read and out write (0 where
+    the down kernel combines itself)."""
+    gu, dn, cb, cold_bytes, uniq = [], [], [], [], []
     for L, ids in layer_picks:
         H, I, k = L.H, L.I, L.k
         w13 = 2 * I * (H // 2) + 2 * I * (H // 32)
@@ -215,11 +217,13 @@ def layer_bytes(layer_picks) -> dict:
         gu.append(U * w13 + T * H * 2 + P * I * 4)           # + x read, h (hi+lo) write
         if P <= DOWN_COMBINE_MAX_PAIRS:                      # fused down + combine: + h read, out write
             dn.append(U * w2 + P * I * 4 + T * H * 4)
-        else:                                                # + h read, y write
+            cb.append(0)
+        else:                                                # + h read, y write; combine: y read, out write
             dn.append(U * w2 + P * I * 4 + P * H * 4)
+            cb.append(P * H * 4 + T * H * 4)
         cold_bytes.append(sum(1 for e in np.unique(ids) if L.slot_np[e] < 0) * L.B)
         uniq.append(U)
-    return {"gate_up": float(np.mean(gu)), "down": float(np.mean(dn)),
+    return {"gate_up": float(np.mean(gu)), "down": float(np.mean(dn)), "combine": float(np.mean(cb)),
             "gather_cold": float(np.mean(cold_bytes)), "unique": float(np.mean(uniq))}
 
 
@@ -255,7 +259,7 @@ def kernel_table(prof: dict, by: dict) -> dict:
     out = {}
     for k, (n, us) in sorted(prof.items()):
         out[k] = {"launches": n, "mean_us": round(us, 3), "us_per_forward": round(n * us / per, 3)}
-    for role in ("gate_up", "down", "gather_cold"):
+    for role in ("gate_up", "down", "combine", "gather_cold"):
         t = role_us(prof, role)
         if t > 0 and by.get(role):
             out[f"role:{role}"] = {"us_per_forward": round(t, 3), "algorithmic_bytes": int(by[role]),
@@ -360,7 +364,7 @@ def layer_figures(name: str, steps: int, warmup: int, reps: int, use_graph: bool
         dom_us = prof[dom][1]
         achieved = by["gate_up"] / (dom_us * 1e-6) / 1e9
         ffn_us = role_us(prof, "gate_up") + role_us(prof, "down") + role_us(prof, "combine")
-        ffn_gbs = (by["gate_up"] + by["down"]) / (ffn_us * 1e-6) / 1e9
+        ffn_gbs = (by["gate_up"] + by["down"] + by["combine"]) / (ffn_us * 1e-6) / 1e9
         if wl.tokens > 32:
             # prefill: the grouped GEMM is a dense contraction; its bound is
             # the bf16 matrix-core peak.  Algorithmic flops of gate/up: 2*P*H*2I.
@@ -383,7 +387,8 @@ def layer_figures(name: str, steps: int, warmup: int, reps: int, use_graph: bool
         out = {"tokens_per_s": round(steps * wl.tokens / med, 2), "ms_per_step": round(1e3 * med / steps, 5),
                "steps": steps, "repeats": rep, "graph": graphed, "mean_distinct_experts": round(by["unique"], 2),
                "roofline": roofline,
-               "ffn": {"kernels": [dom, dn], "us": round(ffn_us, 3), "hbm_GB_per_s": round(ffn_gbs, 1),
+               "ffn": {"kernels": [dom, dn] + sorted(k for k in prof if kernel_role(k) == "combine"),
+                       "us": round(ffn_us, 3), "hbm_GB_per_s": round(ffn_gbs, 1),
                        "frac": round(ffn_gbs / HBM_PEAK_GBS, 4)},
                "kernels": kernels, "_wl": wl}
         out.update(extra)
@@ -569,7 +574,7 @@ def measure_ffn_batches(batches=(1, 8, 32), layers: int = 4, reps: int = 10) -> 
             ffn_runs = [x["gate_up"] + x["down"] + x["combine"] for x in runs]
             by = layer_bytes(picks)
             ffn_us = us["gate_up"] + us["down"] + us["combine"]
-            gbs = (by["gate_up"] + by["down"]) / (ffn_us * 1e-6) / 1e9
+            gbs = (by["gate_up"] + by["down"] + by["combine"]) / (ffn_us * 1e-6) / 1e9
             out[f"batch{T}"] = {
                 "tokens": T, "mean_distinct_experts": round(by["unique"], 2),
                 "gate_up_us": round(us["gate_up"], 3), "down_us": round(us["down"], 3),
@@ -1161,7 +1166,7 @@ def measure_stack(name: str, steps: int, warmup: int, use_graph: bool, one_token
                              "agree_within_2pct": spread(reps) <= AGREE},
                  "distinct_cold_pools": S.distinct_host_pools,
                  "mean_distinct_experts_per_layer": round(by["unique"], 2),
-                 "ffn_hbm_GB_per_s": round((by["gate_up"] + by["down"]) / (ffn_us * 1e-6) / 1e9, 1),
+                 "ffn_hbm_GB_per_s": round((by["gate_up"] + by["down"] + by["combine"]) / (ffn_us * 1e-6) / 1e9, 1),
                  "kernels_per_layer": kt}
         if "gather_cold" in prof and by["gather_cold"] > 0:
             entry["gather_link_GB_per_s"] = round(by["gather_cold"] / (role_us(prof, "gather_cold") * 1e-6) / 1e9, 2)
