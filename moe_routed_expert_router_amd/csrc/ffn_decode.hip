@@ -81,6 +81,7 @@ constexpr int kWideTokens = 8;       // tokens from which down blocks take more 
 // two are 3-10% faster from 16 to 32.
 constexpr int kGateUpWideTokens = 12;
 constexpr int kDmaRows = 8;          // first-pass token rows staged by LDS DMA
+constexpr int kFusedCombineTokens = 16;   // tokens below which the down blocks combine
 
 // The distinct expert of this block for an FFN part (kPartAll / Hot / Cold)
 // and its blob address, pair count and run start; false when the block has
@@ -115,6 +116,106 @@ __device__ __forceinline__ bool part_expert(const GroupView &gv, int part, PartE
     pe.n = n;
     pe.q0 = q0;
     return true;
+}
+
+// ---------------------------- weighted combine ------------------------------
+// out[t] = sum over the token's valid picks j, in pick order, of w[t][j] *
+// y[t*k+j] (the output of the token's j-th pair), accumulated in fp32.  Picks
+// with an id outside [0, E) are skipped.
+struct CombineOut {
+    const int32_t *ids;
+    const float *w;
+    int T, k, E, out_bf16;
+    void *out;
+    int fuse;   // the down blocks combine (else a combine launch follows them)
+};
+
+// y stores and loads that are coherent across the XCDs' L2s (device scope):
+// the combine of a row tile reads pairs written by blocks on other XCDs.
+__device__ __forceinline__ void store4_dev(float *p, float4 v) {
+    uint64_t *q = reinterpret_cast<uint64_t *>(p);
+    const uint64_t lo = (uint64_t)__float_as_uint(v.x) | ((uint64_t)__float_as_uint(v.y) << 32);
+    const uint64_t hi = (uint64_t)__float_as_uint(v.z) | ((uint64_t)__float_as_uint(v.w) << 32);
+    __hip_atomic_store(q, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float4 load4_dev(const float *p) {
+    const uint64_t *q = reinterpret_cast<const uint64_t *>(p);
+    const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_float4(__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
+                       __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32)));
+}
+
+// Combined columns [4*c4, 4*c4 + 4) of token t.  The ids, weights and y
+// columns of up to 8 picks are loaded together with no branch between them
+// (picks past k re-read pick k-1, and an invalid pick's row, never written,
+// is read and dropped), so one wait covers them all; the sums are added in
+// pick order.
+template <bool kDev>
+__device__ __forceinline__ float4 combine4(const float *__restrict__ y, const CombineOut &co, int H, int t,
+                                           int c4) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j0 = 0; j0 < co.k; j0 += 8) {
+        float4 v[8];
+        float wv[8];
+        int id[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const size_t q = (size_t)t * co.k + (j0 + u < co.k ? j0 + u : co.k - 1);
+            id[u] = co.ids[q];
+            wv[u] = co.w[q];
+            const float *src = y + q * H + 4 * (size_t)c4;
+            v[u] = kDev ? load4_dev(src) : *reinterpret_cast<const float4 *>(src);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (j0 + u >= co.k || id[u] < 0 || id[u] >= co.E) continue;
+            acc.x += wv[u] * v[u].x;
+            acc.y += wv[u] * v[u].y;
+            acc.z += wv[u] * v[u].z;
+            acc.w += wv[u] * v[u].w;
+        }
+    }
+    return acc;
+}
+
+__device__ __forceinline__ void store_out4(const CombineOut &co, int H, int t, int c4, float4 acc) {
+    if (co.out_bf16) {
+        const uint32_t b[4] = {f32_to_bf16_bits(acc.x), f32_to_bf16_bits(acc.y), f32_to_bf16_bits(acc.z),
+                               f32_to_bf16_bits(acc.w)};
+        reinterpret_cast<uint2 *>(static_cast<uint16_t *>(co.out) + (size_t)t * H)[c4] = pack_bf16x4(b);
+    } else {
+        reinterpret_cast<float4 *>(static_cast<float *>(co.out) + (size_t)t * H)[c4] = acc;
+    }
+}
+
+// Output rows [row0, row0 + nrows) of every token, by the whole block.
+__device__ __forceinline__ void combine_rows(const float *__restrict__ y, const CombineOut &co, int H, int row0,
+                                             int nrows) {
+    const int per_t = nrows / 4;
+    for (int i = threadIdx.x; i < co.T * per_t; i += blockDim.x) {
+        const int t = i / per_t, c4 = row0 / 4 + i % per_t;
+        store_out4(co, H, t, c4, combine4<true>(y, co, H, t, c4));
+    }
+}
+
+// Called by every thread of a down block once its y stores are issued (with
+// store4_dev): counts the block in its row tile's counter and, in the block
+// that completes the tile (one per distinct expert), combines the tile.  Each
+// thread waits for its own stores to be acknowledged at device scope before
+// the block counts itself, so the last block sees every pair's rows.  `flag`:
+// one int of LDS that no thread reads any more.
+__device__ __forceinline__ void arrive_combine(const GroupView &gv, const CombineOut &co, const float *y, int H,
+                                               int row0, int nrows, int *flag) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int done = __hip_atomic_fetch_add(gv.sync + blockIdx.x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag = done == gv.nuniq[0] - 1;
+    }
+    __syncthreads();
+    if (*flag) combine_rows(y, co, H, row0, nrows);
 }
 
 // RT 16-row tiles of one expert in the decode gate/up: the expert's blob at
@@ -270,26 +371,40 @@ __global__ __launch_bounds__(512) void ffn_gate_up_sel(const uint16_t *__restric
 // SIMD): with the LDS of 5 staged rows that is three blocks per CU instead of
 // the two that 81 registers allowed (with the shared hi / lo MFMA, the
 // batch-32 down went from 76 to 68 us).
+// With co.fuse, the block that completes a row tile (the last of the distinct
+// experts, over the hot and cold launches together) also writes the tile's
+// combined output rows, so no combine launch follows.
 template <int SPW, int RT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SPW <= 8 ? 6 : 4))) void ffn_down_blk(int H, int I, int NT, GroupView gv, int part,
                                                     const uint16_t *__restrict__ hhi,
-                                                    const uint16_t *__restrict__ hlo, float *__restrict__ y) {
+                                                    const uint16_t *__restrict__ hlo, float *__restrict__ y,
+                                                    CombineOut co) {
     extern __shared__ __align__(16) char smem[];
+    const int row0 = blockIdx.x * (16 * RT);
     PartExpert pe;
-    if (!part_expert(gv, part, pe)) return;
+    if (!part_expert(gv, part, pe)) {
+        // no valid pick at all: no block arrives below, so the first row of
+        // blocks writes the (zero) output
+        if (co.fuse && blockIdx.y == 0 && gv.nuniq[0] == 0) combine_rows(y, co, H, row0, 16 * RT);
+        return;
+    }
     const uint8_t *base = pe.base;
     const int n = pe.n, q0 = pe.q0;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
     const int nw = blockDim.x >> 6;
     const int rt = wave % RT, slice = wave / RT;
-    const int row0 = blockIdx.x * (16 * RT);
     const BlobLayout L = BlobLayout::make(H, I);
 
     if (base == nullptr) {   // unusable residency entry: its pairs contribute zero
         for (int i = tid; i < n * 4 * RT; i += blockDim.x) {
             const int p = gv.plist[q0 + i / (4 * RT)];
-            reinterpret_cast<float4 *>(y + (size_t)p * H + row0)[i % (4 * RT)] = make_float4(0.f, 0.f, 0.f, 0.f);
+            float *dst = y + (size_t)p * H + row0 + 4 * (i % (4 * RT));
+            if (co.fuse)
+                store4_dev(dst, make_float4(0.f, 0.f, 0.f, 0.f));
+            else
+                *reinterpret_cast<float4 *>(dst) = make_float4(0.f, 0.f, 0.f, 0.f);
         }
+        if (co.fuse) arrive_combine(gv, co, y, H, row0, 16 * RT, reinterpret_cast<int *>(smem));
         return;
     }
     const size_t row = (size_t)row0 + rt * 16 + r, nst = I / 128;
@@ -374,10 +489,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SPW <= 8 ? 
             }
             const f32x4 s = sh + sl;
             const int p = gv.plist[q0 + tb + r];
-            *reinterpret_cast<float4 *>(y + (size_t)p * H + row0 + wave * 16 + 4 * g) =
-                make_float4(s[0], s[1], s[2], s[3]);
+            float *dst = y + (size_t)p * H + row0 + wave * 16 + 4 * g;
+            if (co.fuse)
+                store4_dev(dst, make_float4(s[0], s[1], s[2], s[3]));
+            else
+                *reinterpret_cast<float4 *>(dst) = make_float4(s[0], s[1], s[2], s[3]);
         }
     }
+    if (co.fuse) arrive_combine(gv, co, y, H, row0, 16 * RT, reinterpret_cast<int *>(smem));
 }
 
 // ====================== down + combine for a few pairs =======================
@@ -739,35 +858,42 @@ __global__ __launch_bounds__(64) void ffn_down_wave(int H, int I, GroupView gv, 
     }
 }
 
-__global__ __launch_bounds__(256) void ffn_combine(const float *__restrict__ y, const int32_t *__restrict__ ids,
-                                                   const float *__restrict__ w, int T, int H, int E, int k,
-                                                   int out_bf16, void *__restrict__ out) {
+__global__ __launch_bounds__(256) void ffn_combine(const float *__restrict__ y, CombineOut co, int H) {
     const int c4 = blockIdx.x * blockDim.x + threadIdx.x;
     if (c4 * 4 >= H) return;
-    for (int t = blockIdx.y; t < T; t += gridDim.y) {
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int j = 0; j < k; ++j) {
-            const int id = ids[(size_t)t * k + j];
-            if (id < 0 || id >= E) continue;
-            const float wj = w[(size_t)t * k + j];
-            const float4 v = reinterpret_cast<const float4 *>(y + ((size_t)t * k + j) * H)[c4];
-            acc.x += wj * v.x;
-            acc.y += wj * v.y;
-            acc.z += wj * v.z;
-            acc.w += wj * v.w;
-        }
-        if (out_bf16) {
-            const uint32_t b[4] = {f32_to_bf16_bits(acc.x), f32_to_bf16_bits(acc.y), f32_to_bf16_bits(acc.z),
-                                   f32_to_bf16_bits(acc.w)};
-            reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + (size_t)t * H)[c4] = pack_bf16x4(b);
-        } else {
-            reinterpret_cast<float4 *>(static_cast<float *>(out) + (size_t)t * H)[c4] = acc;
-        }
-    }
+    for (int t = blockIdx.y; t < co.T; t += gridDim.y) store_out4(co, H, t, c4, combine4<false>(y, co, H, t, c4));
 }
 
 // ================================ launchers =================================
 namespace {
+
+// Whether the decode down blocks combine (the block completing a row tile
+// adds it up) rather than a combine launch following them.  Each block then
+// waits for its y stores and a counter round trip before it ends: measured
+// (FFN alone, Zipf routing), 8 tokens 72.2 against 73.9 us, 32 tokens 174.1
+// against 171.4 us (with ~4600 blocks the tails cost more than the launch).
+bool down_combines(int T) { return T < kFusedCombineTokens; }
+
+size_t down_combine_lds(int T, int k, int H, int I);
+
+// Completion counter words the down blocks of a decode FFN use (one per row
+// tile of at least 32 rows), 0 when they do not combine.
+int down_counter_words(const FfnArgs &a) {
+    return !down_combine_lds(a.T, a.k, a.H, a.I) && down_combines(a.T) ? a.H / 32 : 0;
+}
+
+CombineOut combine_out(const FfnArgs &a) {
+    CombineOut c;
+    c.ids = a.ids;
+    c.w = a.w;
+    c.T = a.T;
+    c.k = a.k;
+    c.E = a.E;
+    c.out_bf16 = a.out_bf16;
+    c.out = a.out;
+    c.fuse = down_combines(a.T);
+    return c;
+}
 
 // Smallest steps-per-wave in {1,2,4,8,16} dividing `steps` with at most
 // max_slices slices; 0 if none.
@@ -826,7 +952,7 @@ void launch_down_blk(const FfnArgs &a, const GroupView &gv, int part, const uint
     const size_t lds = (size_t)2 * NT * row_bytes + (size_t)RT * slices * 64 * 16;
     MOE_LAUNCH(part_name(part, "ffn_down_blk", "ffn_down_blk_hot", "ffn_down_blk_cold"),
                (ffn_down_blk<SPW, RT>), dim3(a.H / (16 * RT), umax), dim3(64 * RT * slices), lds, st, a.H,
-               a.I, NT, gv, part, hhi, hlo, y);
+               a.I, NT, gv, part, hhi, hlo, y, combine_out(a));
 }
 
 void gate_up_blk(const FfnArgs &a, const GroupView &gv, int part, uint16_t *hhi, uint16_t *hlo, int umax,
@@ -915,8 +1041,7 @@ void launch_down_combine(const FfnArgs &a, const GroupView &gv, const uint16_t *
 void launch_combine(const FfnArgs &a, const float *y, hipStream_t st) {
     const int n4 = a.H / 4;
     const int ty = a.T < 65535 ? a.T : 65535;
-    MOE_LAUNCH("ffn_combine", ffn_combine, dim3((n4 + 255) / 256, ty), dim3(256), 0, st, y, a.ids, a.w, a.T, a.H,
-               a.E, a.k, a.out_bf16, a.out);
+    MOE_LAUNCH("ffn_combine", ffn_combine, dim3((n4 + 255) / 256, ty), dim3(256), 0, st, y, combine_out(a), a.H);
 }
 
 }  // namespace
@@ -990,6 +1115,7 @@ hipError_t launch_ffn(const FfnArgs &a, char *ws, const WsLayout &L, hipStream_t
             return hipGetLastError();
         }
         down_blk(a, gv, kPartAll, hhi, hlo, y, umax, st);
+        if (down_combines(a.T)) return hipGetLastError();
     } else {
         const int sgu = a.H / 128;
         const dim3 ggu(a.I / 16, umax);
@@ -1018,7 +1144,8 @@ hipError_t launch_ffn_select(const FfnArgs &a, const float *z, int renorm, int32
                              const GroupArgs &g, char *ws, const WsLayout &L, hipStream_t st) {
     const GroupView gv = group_view(ws, L);
     const GroupOut o = GroupOut::at(ws, L);
-    const SelectArgs sa = select_args(z, a.T, a.k, renorm, ids, w, g);
+    SelectArgs sa = select_args(z, a.T, a.k, renorm, ids, w, g);
+    sa.nsync = down_counter_words(a);
     const size_t P = (size_t)a.T * a.k;
     const int umax = (int)((size_t)a.E < P ? (size_t)a.E : P);
     uint16_t *hhi = reinterpret_cast<uint16_t *>(ws + L.hbuf);
@@ -1029,7 +1156,7 @@ hipError_t launch_ffn_select(const FfnArgs &a, const float *z, int renorm, int32
         launch_down_combine(a, gv, hhi, hlo, st);
     } else {
         down_blk(a, gv, kPartAll, hhi, hlo, y, umax, st);
-        launch_combine(a, y, st);
+        if (!down_combines(a.T)) launch_combine(a, y, st);
     }
     return hipGetLastError();
 }
@@ -1038,7 +1165,8 @@ hipError_t launch_ffn_select_hot(const FfnArgs &a, const float *z, int renorm, i
                                  const GroupArgs &g, char *ws, const WsLayout &L, hipStream_t st) {
     const GroupView gv = group_view(ws, L);
     const GroupOut o = GroupOut::at(ws, L);
-    const SelectArgs sa = select_args(z, a.T, a.k, renorm, ids, w, g);
+    SelectArgs sa = select_args(z, a.T, a.k, renorm, ids, w, g);
+    sa.nsync = down_counter_words(a);
     const size_t P = (size_t)a.T * a.k;
     const int umax = (int)((size_t)a.E < P ? (size_t)a.E : P);
     uint16_t *hhi = reinterpret_cast<uint16_t *>(ws + L.hbuf);
@@ -1064,10 +1192,14 @@ hipError_t launch_ffn_part(const FfnArgs &a, int part, int umax_part, char *ws, 
         gate_up_blk(a, gv, part, hhi, hlo, umax_part, st);
         if (!fused) down_blk(a, gv, part, hhi, hlo, y, umax_part, st);
     }
+    // below kFusedCombineTokens the down blocks of the two parts combine
+    // (without a cold launch, those of the hot part alone cover every
+    // distinct expert; the combine launch then only writes the same values
+    // again)
     if (part == kPartCold) {
         if (fused)
             launch_down_combine(a, gv, hhi, hlo, st);
-        else
+        else if (!down_combines(a.T) || umax_part == 0)
             launch_combine(a, y, st);
     }
     return hipGetLastError();

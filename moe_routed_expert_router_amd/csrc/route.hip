@@ -341,6 +341,7 @@ SelectArgs select_args(const float *z, int T, int k, int renorm, int32_t *ids, f
     s.hot_base = a.hot_base;
     s.scratch = a.scratch;
     s.blob_bytes = a.blob_bytes;
+    s.nsync = WsLayout::kSyncWords;
     return s;
 }
 

@@ -16,6 +16,7 @@ struct SelectArgs {
     int n_hot, n_cold;
     const uint8_t *hot_base, *scratch;
     size_t blob_bytes;
+    int nsync;        // completion counter words to clear when publishing
 };
 
 // LDS of select_group_block: P ints each for sid and sflag, T ints for the
@@ -40,6 +41,8 @@ __device__ __forceinline__ void select_group_block(const SelectArgs &a, const Gr
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
     const int k = a.k, bd = blockDim.x;
     if (tid == 0) s.sinfo[0] = 0;
+    if (publish)   // the down blocks' per-row-tile completion counters
+        for (int i = tid; i < a.nsync; i += bd) o.sync[i] = 0;
     // the residency entries are requested before the logits and land in LDS
     // after the top-k, so looking up the picked experts' entries costs no
     // round trip of its own
