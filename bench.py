@@ -33,6 +33,7 @@ METRIC = "routed-expert layer tokens/s + achieved HBM & host-link GB/s at batch 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFS = 2500.0      # MI355X dense bf16 matrix cores, 2.5 PFLOP/s
 DOWN_COMBINE_MAX_PAIRS = 8       # T*k up to which the library fuses the down projection and the combine
+DOWN_BLOCKS_COMBINE_TOKENS = 16  # tokens below which the decode down blocks combine their row tiles themselves
 LINK_PEAK_GBS = 64.0             # PCIe Gen5 x16, one direction
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -217,6 +218,9 @@ def layer_bytes(layer_picks) -> dict:
         gu.append(U * w13 + T * H * 2 + P * I * 4)           # + x read, h (hi+lo) write
         if P <= DOWN_COMBINE_MAX_PAIRS:                      # fused down + combine: + h read, out write
             dn.append(U * w2 + P * I * 4 + T * H * 4)
+            cb.append(0)
+        elif T < DOWN_BLOCKS_COMBINE_TOKENS:                 # + h read, y write, and the combine's y read, out write
+            dn.append(U * w2 + P * I * 4 + P * H * 4 + P * H * 4 + T * H * 4)
             cb.append(0)
         else:                                                # + h read, y write; combine: y read, out write
             dn.append(U * w2 + P * I * 4 + P * H * 4)

@@ -403,9 +403,11 @@ def test_bf16_output_is_rounded_fp32():
     assert torch.equal(b, f.to(torch.bfloat16))
 
 
-@pytest.mark.parametrize("T,bad_pos", [(6, [(1, 0), (3, 1)]), (2, [(0, 1), (1, 0)])])
+@pytest.mark.parametrize("T,bad_pos", [(6, [(1, 0), (3, 1)]), (2, [(0, 1), (1, 0)]), (20, [(0, 1), (19, 0)])])
 def test_invalid_ids_contribute_zero(T, bad_pos):
-    """T=2 (4 pairs) runs the fused down + combine kernel, T=6 the separate ones."""
+    """T=2 (4 pairs) runs the fused down + combine kernel, T=6 the down blocks
+    that combine their row tiles themselves, T=20 the down blocks and then
+    the combine launch."""
     L = Layer(gen.workload("tiny"), T=T)
     ids_g, w_g, _ = route_on_gpu(L)
     bad = ids_g.copy()
@@ -424,10 +426,11 @@ def test_invalid_ids_contribute_zero(T, bad_pos):
     check_out(out.cpu().numpy(), want)
 
 
-@pytest.mark.parametrize("T", [1, 6])
+@pytest.mark.parametrize("T", [1, 6, 20])
 def test_unusable_residency_entry_contributes_zero(T):
     """A device residency entry outside [0, n_hot) makes that expert's pairs
-    contribute zero (fused down + combine at T=1, separate kernels at T=6)."""
+    contribute zero (fused down + combine at T=1, down blocks that combine
+    at T=6, down blocks and a combine launch at T=20)."""
     L = Layer(gen.workload("tiny"), T=T)
     ids_g, w_g, _ = route_on_gpu(L)
     e_bad = int(ids_g[0, 0])
@@ -443,6 +446,24 @@ def test_unusable_residency_entry_contributes_zero(T):
     y[ids_g == e_bad] = 0
     from oracle.ffn import combine
     check_out(out.cpu().numpy(), combine(w_g, y))
+
+
+@pytest.mark.parametrize("T", [2, 6, 20])
+def test_all_ids_invalid_give_zero_output(T):
+    """With no valid pick there is no distinct expert, so no down block counts
+    itself in: the output must still be written, as zeros, by every path
+    (fused down + combine, down blocks that combine, combine launch), also
+    over a workspace that the previous call left with live counters."""
+    L = Layer(gen.workload("tiny"), T=T)
+    ids_g, w_g, _ = route_on_gpu(L)
+    out = torch.full((L.T, L.H), 7.0, dtype=torch.float32, device="cuda")
+    moe.moe_expert_ffn(L.shape, L.x, torch.from_numpy(ids_g).cuda(), torch.from_numpy(w_g).cuda(), L.residency,
+                       out, L.ws)
+    bad = np.where(np.arange(ids_g.size).reshape(ids_g.shape) % 2 == 0, -1, L.E).astype(ids_g.dtype)
+    moe.moe_expert_ffn(L.shape, L.x, torch.from_numpy(bad).cuda(), torch.from_numpy(w_g).cuda(), L.residency,
+                       out, L.ws)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0
 
 
 @pytest.mark.parametrize("mode", ["invalid_ids", "unusable_entry"])
