@@ -870,8 +870,9 @@ namespace {
 // Whether the decode down blocks combine (the block completing a row tile
 // adds it up) rather than a combine launch following them.  Each block then
 // waits for its y stores and a counter round trip before it ends: measured
-// (FFN alone, Zipf routing), 8 tokens 72.2 against 73.9 us, 32 tokens 174.1
-// against 171.4 us (with ~4600 blocks the tails cost more than the launch).
+// (FFN alone, Zipf routing), 8 tokens 72.2 against 73.9 us; 16, 24 and 32
+// tokens 114.2, 147.9 and 174.1 against 113.1, 145.8 and 171.4 us (with
+// thousands of blocks the tails cost more than the launch).
 bool down_combines(int T) { return T < kFusedCombineTokens; }
 
 size_t down_combine_lds(int T, int k, int H, int I);
